@@ -1,0 +1,306 @@
+"""fp64 CPU oracle for the DFlash drafter's block attention.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, by the package smoke check
+and by the benchmark's CPU-baseline leg, never by the product path.
+
+What is computed (TensorRT-LLM PR #20532 "Share Kimi K3 FP4 modeling and add
+NVFP4 support on SM103", Conversation, the commit that adds k3_drafter_attn
+and k3_drafter_attn_qknorm, and the next commit that adds their contracts):
+
+* Up to 8 requests each bring a draft block of up to 8 tokens.  Every block
+  attends densely -- no causal mask -- to its request's paged context and to
+  its own K/V, which come from the packed qkv rows and are never written to
+  the page pool.
+* GQA with 6 query heads per KV head, head_dim 64, HND pages of 64 tokens.
+* k3_drafter_attn takes q/k already normalised and rotated;
+  k3_drafter_attn_qknorm applies the per-head q/k RMSNorm (eps 1e-5) and the
+  NeoX rotary embedding (base 10000) itself.
+
+The method is an exact reformulation of softmax attention, so this oracle is
+that definition written out in float64 on the exact bf16 input values, with
+nothing rounded.  Readings of points the pages leave open (the same ones the
+library's header documents):
+
+* qkv row ``r*T + t`` holds ``[q heads | k heads | v heads]``, 64 columns each.
+* Query head ``h`` uses KV head ``h // 6`` (contiguous GQA groups).
+* Page ``p`` of a pool holds ``[Hkv][64 slots][64 dims]``; context token ``c``
+  of request ``r`` is slot ``c % 64`` of page ``page_table[r, c // 64]``.
+  Only the first ``ceil(L/64)`` entries of a page-table row are meaningful;
+  slots past ``L`` in the last page are not part of the input.
+* A request may bring fewer than T tokens (``block_lens``); its rows past that
+  length are neither keys nor outputs and their outputs are zero.
+* RMSNorm is ``x * w / sqrt(mean(x^2) + eps)`` over one head's 64 values with
+  one weight vector for all q heads and one for all k heads.
+* NeoX rotation pairs dimension ``i`` with ``i + 32`` at angle
+  ``pos * base**(-2i/64)``; only the block's q and k are rotated, never v and
+  never the context (the pool holds keys that are already processed).
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, Optional, Tuple
+
+import numpy as np
+
+HEAD_DIM = 64
+PAGE = 64
+GQA = 6
+
+
+class OracleContractError(ValueError):
+    """An input outside the operation's contract (the library clamps and flags these)."""
+
+
+# --------------------------------------------------------------------------------------
+# q/k preprocessing (the qknorm variant)
+# --------------------------------------------------------------------------------------
+
+def rms_norm(x: np.ndarray, w: np.ndarray, eps: float) -> np.ndarray:
+    """Per-head RMSNorm over the last axis (64 values of one head).
+
+    PR #20532, commit adding fused_qk_norm_rope's drafter cell: eps 1e-5,
+    head_dim 64; the attention commit names a per-head q/k RMSNorm.
+    ``x * w / sqrt(mean(x**2) + eps)``.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x * np.asarray(w, dtype=np.float64) / np.sqrt(ms + eps)
+
+
+def rope_inv_freq(base: float, dim: int = HEAD_DIM) -> np.ndarray:
+    """Rotary frequencies ``base**(-2i/dim)`` for ``i < dim/2`` (base 10000 in the cell)."""
+    i = np.arange(dim // 2, dtype=np.float64)
+    return np.power(float(base), -2.0 * i / dim)
+
+
+def rope_neox(x: np.ndarray, pos, base: float) -> np.ndarray:
+    """NeoX ("rotate half") rotary embedding over the last axis.
+
+    PR #20532, fused_qk_norm_rope drafter cell: NeoX style, base 10000.
+    Dimension ``i`` pairs with ``i + dim/2``; the pair is turned by the angle
+    ``pos * inv_freq[i]``.  ``pos`` broadcasts against ``x[..., 0]``.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    half = x.shape[-1] // 2
+    ang = np.asarray(pos, dtype=np.float64)[..., None] * rope_inv_freq(base, x.shape[-1])
+    c, s = np.cos(ang), np.sin(ang)
+    x1, x2 = x[..., :half], x[..., half:]
+    return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
+
+
+# --------------------------------------------------------------------------------------
+# paged context
+# --------------------------------------------------------------------------------------
+
+def gather_context(k_pool: np.ndarray, v_pool: np.ndarray, table_row: np.ndarray,
+                   L: int, g: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Context K and V of one request and KV head, in logical token order.
+
+    Walks the page-table row page by page: logical page ``j`` is physical page
+    ``table_row[j]``, holding tokens ``64*j .. 64*j+63`` (HND: head, slot, dim).
+    Only the first ``L - 64*j`` slots of the last page are taken.
+    """
+    P = k_pool.shape[0]
+    npg = -(-L // PAGE)
+    ks, vs = [], []
+    for j in range(npg):
+        phys = int(table_row[j])
+        if not 0 <= phys < P:
+            raise OracleContractError(f"page id {phys} out of range [0, {P})")
+        n = min(PAGE, L - PAGE * j)
+        ks.append(k_pool[phys, g, :n, :])
+        vs.append(v_pool[phys, g, :n, :])
+    if not ks:
+        z = np.zeros((0, k_pool.shape[-1]))
+        return z, z.copy()
+    return np.concatenate(ks, axis=0).astype(np.float64), np.concatenate(vs, axis=0).astype(np.float64)
+
+
+# --------------------------------------------------------------------------------------
+# attention
+# --------------------------------------------------------------------------------------
+
+def kv_head_of(h: int) -> int:
+    """GQA: query head ``h`` reads KV head ``h // 6`` (6 query heads per KV head)."""
+    return h // GQA
+
+
+def q_cols(h: int, Hq: int, Hkv: int) -> slice:
+    """qkv columns of query head ``h``."""
+    return slice(h * HEAD_DIM, (h + 1) * HEAD_DIM)
+
+
+def k_cols(g: int, Hq: int, Hkv: int) -> slice:
+    """qkv columns of the block's key head ``g`` (after the Hq query heads)."""
+    return slice((Hq + g) * HEAD_DIM, (Hq + g + 1) * HEAD_DIM)
+
+
+def v_cols(g: int, Hq: int, Hkv: int) -> slice:
+    """qkv columns of the block's value head ``g`` (after the q and k heads)."""
+    return slice((Hq + Hkv + g) * HEAD_DIM, (Hq + Hkv + g + 1) * HEAD_DIM)
+
+
+def _softmax_attend(q: np.ndarray, keys: np.ndarray, vals: np.ndarray, scale: float):
+    """Dense softmax attention of query rows over all keys (no mask).
+
+    Stable form: subtract each row's maximum score before exponentiating.
+    Returns the outputs and the softmax weights.
+    """
+    s = scale * (q @ keys.T)
+    s = s - s.max(axis=-1, keepdims=True)
+    e = np.exp(s)
+    p = e / e.sum(axis=-1, keepdims=True)
+    return p @ vals, p
+
+
+def _check_shapes(qkv, k_pool, v_pool, page_table, context_lens, block_lens,
+                  Hq: int, Hkv: int, T: int):
+    if Hkv < 1 or Hq != GQA * Hkv:
+        raise OracleContractError(f"need Hq == 6*Hkv, got {Hq}/{Hkv}")
+    R = len(context_lens)
+    if not (1 <= R <= 8 and 1 <= T <= 8):
+        raise OracleContractError(f"R={R}, T={T} outside 1..8")
+    if qkv.shape[0] != R * T or qkv.shape[1] < (Hq + 2 * Hkv) * HEAD_DIM:
+        raise OracleContractError("qkv shape")
+    if k_pool.shape[1:] != (Hkv, PAGE, HEAD_DIM) or v_pool.shape != k_pool.shape:
+        raise OracleContractError("pool shape")
+    stride = page_table.shape[1] if page_table is not None and page_table.ndim == 2 else 0
+    for r in range(R):
+        L = int(context_lens[r])
+        if not 0 <= L <= stride * PAGE:
+            raise OracleContractError(f"context length {L} outside [0, {stride * PAGE}]")
+    if block_lens is not None:
+        for r in range(R):
+            if not 1 <= int(block_lens[r]) <= T:
+                raise OracleContractError("block length outside [1, T]")
+    return R
+
+
+def _run(qkv, k_pool, v_pool, page_table, context_lens, block_lens, Hq, Hkv, T, scale,
+         prep_q, prep_k, return_probs: bool):
+    R = _check_shapes(qkv, k_pool, v_pool, page_table, context_lens, block_lens, Hq, Hkv, T)
+    D = HEAD_DIM
+    qkv = np.asarray(qkv, dtype=np.float64)
+    out = np.zeros((R * T, Hq * D), dtype=np.float64)
+    probs: Dict[Tuple[int, int, int], np.ndarray] = {}
+    for r in range(R):
+        L = int(context_lens[r])
+        b = T if block_lens is None else int(block_lens[r])
+        rows = slice(r * T, r * T + b)
+        kv = {}
+        for g in range(Hkv):
+            kc, vc = gather_context(k_pool, v_pool, page_table[r] if L else None, L, g)
+            kb = prep_k(qkv[rows, k_cols(g, Hq, Hkv)], r, b)
+            vb = qkv[rows, v_cols(g, Hq, Hkv)]
+            kv[g] = (np.concatenate([kc, kb], axis=0), np.concatenate([vc, vb], axis=0))
+        for h in range(Hq):
+            keys, vals = kv[kv_head_of(h)]
+            q = prep_q(qkv[rows, q_cols(h, Hq, Hkv)], r, b)
+            o, p = _softmax_attend(q, keys, vals, scale)
+            out[rows, h * D:(h + 1) * D] = o
+            if return_probs:
+                for t in range(b):
+                    probs[(r, h, t)] = p[t]
+    return (out, probs) if return_probs else out
+
+
+def drafter_attn(qkv, k_pool, v_pool, page_table, context_lens, block_lens=None, *,
+                 num_q_heads: int, num_kv_heads: int, tokens_per_block: int,
+                 scale: Optional[float] = None, return_probs: bool = False, **_unused):
+    """k3_drafter_attn: block attention over paged context + own block, q/k used as given.
+
+    Returns ``out`` float64 ``[R*T, Hq*64]`` (and the softmax weights per
+    (request, head, token) when ``return_probs``).
+    """
+    if scale is None:
+        scale = 1.0 / math.sqrt(HEAD_DIM)
+    ident = lambda x, r, b: np.asarray(x, dtype=np.float64)
+    return _run(qkv, k_pool, v_pool, page_table, context_lens, block_lens, num_q_heads,
+                num_kv_heads, tokens_per_block, scale, ident, ident, return_probs)
+
+
+def drafter_attn_qknorm(qkv, k_pool, v_pool, page_table, context_lens, block_lens=None, *,
+                        positions, q_norm_weight, k_norm_weight, num_q_heads: int,
+                        num_kv_heads: int, tokens_per_block: int, scale: Optional[float] = None,
+                        eps: float = 1e-5, rope_base: float = 10000.0,
+                        return_probs: bool = False, **_unused):
+    """k3_drafter_attn_qknorm: RMSNorm then NeoX RoPE on the block's q and k, then attention.
+
+    The block's v and the whole paged context are used as stored.  Positions
+    are read per token (``positions[r*T + t]``).
+    """
+    if scale is None:
+        scale = 1.0 / math.sqrt(HEAD_DIM)
+    T = tokens_per_block
+    pos = np.asarray(positions, dtype=np.int64)
+
+    def prep(w):
+        def f(x, r, b):
+            return rope_neox(rms_norm(x, w, eps), pos[r * T:r * T + b], rope_base)
+        return f
+
+    return _run(qkv, k_pool, v_pool, page_table, context_lens, block_lens, num_q_heads,
+                num_kv_heads, T, scale, prep(q_norm_weight), prep(k_norm_weight), return_probs)
+
+
+def drafter_attn_split_merge(qkv, k_pool, v_pool, page_table, context_lens, block_lens=None, *,
+                             num_splits: int, num_q_heads: int, num_kv_heads: int,
+                             tokens_per_block: int, scale: Optional[float] = None,
+                             positions=None, q_norm_weight=None, k_norm_weight=None,
+                             eps: float = 1e-5, rope_base: float = 10000.0,
+                             qknorm: bool = False, **_unused):
+    """The same attention computed split-KV (flash-decoding) style.
+
+    The context pages of a request are cut into ``num_splits`` consecutive page
+    ranges; the own block is one more range.  Each range yields its running
+    maximum ``m``, weight sum ``l`` and unnormalised output ``O``; the ranges
+    are merged by rescaling with ``exp(m_s - M)``, ``M = max_s m_s``.  This is
+    the algebra of the split-combine pass, checked here against the plain
+    definition independently of any GPU code.
+    """
+    if scale is None:
+        scale = 1.0 / math.sqrt(HEAD_DIM)
+    Hq, Hkv, T, D = num_q_heads, num_kv_heads, tokens_per_block, HEAD_DIM
+    R = _check_shapes(qkv, k_pool, v_pool, page_table, context_lens, block_lens, Hq, Hkv, T)
+    qkv = np.asarray(qkv, dtype=np.float64)
+    if qknorm:
+        pos = np.asarray(positions, dtype=np.int64)
+        pq = lambda x, r, b: rope_neox(rms_norm(x, q_norm_weight, eps), pos[r * T:r * T + b], rope_base)
+        pk = lambda x, r, b: rope_neox(rms_norm(x, k_norm_weight, eps), pos[r * T:r * T + b], rope_base)
+    else:
+        pq = pk = lambda x, r, b: x
+    stride = page_table.shape[1] if page_table is not None and page_table.ndim == 2 else 0
+    per = max(1, -(-stride // num_splits))
+    out = np.zeros((R * T, Hq * D))
+    for r in range(R):
+        L = int(context_lens[r])
+        b = T if block_lens is None else int(block_lens[r])
+        rows = slice(r * T, r * T + b)
+        rng_of = {}
+        for g in range(Hkv):
+            kc, vc = gather_context(k_pool, v_pool, page_table[r] if L else None, L, g)
+            kb = pk(qkv[rows, k_cols(g, Hq, Hkv)], r, b)
+            vb = qkv[rows, v_cols(g, Hq, Hkv)]
+            rng_of[g] = [(kc[s * per * PAGE:(s + 1) * per * PAGE], vc[s * per * PAGE:(s + 1) * per * PAGE])
+                         for s in range(num_splits)] + [(kb, vb)]
+        for h in range(Hq):
+            ranges = rng_of[kv_head_of(h)]
+            q = pq(qkv[rows, q_cols(h, Hq, Hkv)], r, b)
+            parts = []
+            for kk, vv in ranges:
+                if kk.shape[0] == 0:
+                    parts.append((np.full(b, -np.inf), np.zeros(b), np.zeros((b, D))))
+                    continue
+                s = scale * (q @ kk.T)
+                m = s.max(axis=-1)
+                e = np.exp(s - m[:, None])
+                parts.append((m, e.sum(axis=-1), e @ vv))
+            M = np.max([p[0] for p in parts], axis=0)
+            num = np.zeros((b, D))
+            den = np.zeros(b)
+            for m, l, o in parts:
+                w = np.where(np.isfinite(m), np.exp(m - M), 0.0)
+                num += w[:, None] * o
+                den += w * l
+            out[rows, h * D:(h + 1) * D] = num / den[:, None]
+    return out

@@ -1,0 +1,145 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that a pin catches each.
+
+Every mutation below is a slip one could make writing the oracle from the
+pages: a dropped term, a wrong sign, index or offset, a transposed operand.
+The pins in test_oracle_pins.py must turn at least one of them red.
+"""
+import numpy as np
+import pytest
+import torch
+
+import drafter_synth as ds
+import oracle
+import oracle.drafter_attn_oracle as mod
+from tests import test_oracle_pins as pins
+from tests.bruteforce import bruteforce
+
+orig_rms = mod.rms_norm
+orig_rope = mod.rope_neox
+orig_freq = mod.rope_inv_freq
+orig_gather = mod.gather_context
+orig_attend = mod._softmax_attend
+
+
+def _rope_sign(x, pos, base):
+    x = np.asarray(x, dtype=np.float64)
+    ang = np.asarray(pos, dtype=np.float64)[..., None] * orig_freq(base, x.shape[-1])
+    c, s = np.cos(ang), np.sin(ang)
+    x1, x2 = x[..., :32], x[..., 32:]
+    return np.concatenate([x1 * c + x2 * s, x2 * c - x1 * s], axis=-1)
+
+
+def _rope_interleaved(x, pos, base):
+    x = np.asarray(x, dtype=np.float64)
+    ang = np.asarray(pos, dtype=np.float64)[..., None] * orig_freq(base, x.shape[-1])
+    c, s = np.cos(ang), np.sin(ang)
+    x1, x2 = x[..., 0::2], x[..., 1::2]
+    y = np.empty_like(x)
+    y[..., 0::2] = x1 * c - x2 * s
+    y[..., 1::2] = x2 * c + x1 * s
+    return y
+
+
+def _gather_shift_slot(k_pool, v_pool, row, L, g):
+    k, v = orig_gather(k_pool, v_pool, row, L, g)
+    return np.roll(k, 1, axis=0), v
+
+
+def _gather_next_entry(k_pool, v_pool, row, L, g):
+    if row is None:
+        return orig_gather(k_pool, v_pool, row, L, g)
+    return orig_gather(k_pool, v_pool, np.roll(np.asarray(row), -1) % k_pool.shape[0], L, g)
+
+
+def _gather_full_pages_only(k_pool, v_pool, row, L, g):
+    return orig_gather(k_pool, v_pool, row, (L // 64) * 64, g)
+
+
+def _gather_other_head(k_pool, v_pool, row, L, g):
+    return orig_gather(k_pool, v_pool, row, L, (g + 1) % k_pool.shape[1])
+
+
+def _attend_no_scale(q, keys, vals, scale):
+    return orig_attend(q, keys, vals, 1.0)
+
+
+def _attend_wrong_axis(q, keys, vals, scale):
+    s = scale * (q @ keys.T)
+    e = np.exp(s - s.max())
+    p = e / e.sum(axis=0, keepdims=True)
+    return p @ vals, p
+
+
+def _attend_context_only(q, keys, vals, scale):
+    n = max(1, keys.shape[0] - q.shape[0])
+    return orig_attend(q, keys[:n], vals[:n], scale)
+
+
+def _attend_v_is_k(q, keys, vals, scale):
+    return orig_attend(q, keys, keys, scale)
+
+
+MUTATIONS = {
+    "rms_no_eps": ("rms_norm", lambda x, w, eps: orig_rms(x, w, 0.0)),
+    "rms_sum_not_mean": ("rms_norm", lambda x, w, eps: np.asarray(x) * w / np.sqrt(np.sum(np.asarray(x) ** 2, -1, keepdims=True) + eps)),
+    "rms_one_plus_w": ("rms_norm", lambda x, w, eps: orig_rms(x, 1.0 + np.asarray(w), eps)),
+    "rms_no_weight": ("rms_norm", lambda x, w, eps: orig_rms(x, np.ones_like(w), eps)),
+    "rope_sign": ("rope_neox", _rope_sign),
+    "rope_interleaved": ("rope_neox", _rope_interleaved),
+    "rope_pos_plus_one": ("rope_neox", lambda x, pos, base: orig_rope(x, np.asarray(pos) + 1, base)),
+    "rope_exponent": ("rope_inv_freq", lambda base, dim=64: np.power(float(base), -np.arange(dim // 2) / dim)),
+    "rope_base_1000": ("rope_inv_freq", lambda base, dim=64: orig_freq(1000.0, dim)),
+    "gather_slot_shift": ("gather_context", _gather_shift_slot),
+    "gather_next_entry": ("gather_context", _gather_next_entry),
+    "gather_drop_tail": ("gather_context", _gather_full_pages_only),
+    "gather_other_head": ("gather_context", _gather_other_head),
+    "gqa_modulo": ("kv_head_of", lambda h: h % 2),
+    "k_from_v_cols": ("k_cols", lambda g, Hq, Hkv: mod.v_cols(g, Hq, Hkv)),
+    "v_from_k_cols": ("v_cols", lambda g, Hq, Hkv: slice((Hq + g) * 64, (Hq + g + 1) * 64)),
+    "q_head_offset": ("q_cols", lambda h, Hq, Hkv: slice(((h + 1) % Hq) * 64, ((h + 1) % Hq + 1) * 64)),
+    "no_scale": ("_softmax_attend", _attend_no_scale),
+    "softmax_wrong_axis": ("_softmax_attend", _attend_wrong_axis),
+    "drop_block_keys": ("_softmax_attend", _attend_context_only),
+    "values_are_keys": ("_softmax_attend", _attend_v_is_k),
+}
+
+
+def _battery():
+    """Run a cheap set of pins; return the names of those that failed."""
+    failed = []
+    cases = [
+        ds.make_case(2, 3, 12, 2, [65, 130], seed=77, qknorm=True, pool_pages=6),
+        ds.make_case(2, 2, 6, 1, [64, 3], seed=78, qknorm=False, pool_pages=4),
+    ]
+    for i, c in enumerate(cases):
+        try:
+            ref = bruteforce(**c.np_args(), qknorm=c.qknorm)
+            got = pins._oracle(c)
+            if not pins._rel(got, ref) <= pins.TOL:
+                failed.append(f"bruteforce{i}")
+        except Exception:  # any error is a failed pin
+            failed.append(f"bruteforce{i}")
+    for name in ("test_rmsnorm_closed_forms", "test_rope_closed_forms"):
+        try:
+            getattr(pins, name)()
+        except Exception:  # any error is a failed pin
+            failed.append(name)
+    for where in ("first", "tail_slot", "block"):
+        try:
+            pins.test_needle(where)
+        except Exception:  # any error is a failed pin
+            failed.append(f"needle_{where}")
+    return failed
+
+
+def test_battery_green_on_unmutated_oracle():
+    assert _battery() == []
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutation_is_caught(name, monkeypatch):
+    attr, fn = MUTATIONS[name]
+    monkeypatch.setattr(mod, attr, fn)
+    if hasattr(oracle, attr):
+        monkeypatch.setattr(oracle, attr, fn)
+    assert _battery(), f"no pin caught mutation {name}"

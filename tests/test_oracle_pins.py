@@ -1,0 +1,362 @@
+"""Pins of the fp64 oracle against things other than itself (CPU only).
+
+The pages print no worked example for this kernel, so the oracle is pinned by:
+an independently built brute force (one masked softmax over the whole batch),
+torch's float64 scaled_dot_product_attention on gathered tensors, closed forms
+(L=0/T=1, q=0, constant V, needle keys, RMSNorm of a constant vector, rotary
+values at exactly representable frequencies), and invariants (softmax weights
+sum to one, physical page placement, request isolation, poison, composition of
+the qknorm variant, split-merge algebra).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import drafter_synth as ds
+import oracle
+from tests.bruteforce import bruteforce
+
+TOL = 1e-12
+
+
+def _rel(a, b):
+    return float(np.max(np.abs(a - b)) / max(1.0, float(np.max(np.abs(b)))))
+
+
+def _tiny_cases():
+    out = []
+    seed = 11
+    for R in (1, 2, 3):
+        for T in (1, 2, 3):
+            for Hkv in (1, 2):
+                lens = [[0, 1, 63, 64, 65, 130][(R * 7 + T * 3 + i + Hkv) % 6] for i in range(R)]
+                for qk in (False, True):
+                    seed += 1
+                    out.append(ds.make_case(R, T, 6 * Hkv, Hkv, lens, seed=seed,
+                                            stride=max(3, max(-(-L // 64) for L in lens)),
+                                            pool_pages=12, qknorm=qk,
+                                            pos_dtype=torch.int64 if qk else torch.int32))
+    return out
+
+
+def _oracle(case, **kw):
+    a = case.np_args()
+    a.update(kw)
+    if case.qknorm:
+        return oracle.drafter_attn_qknorm(**a)
+    return oracle.drafter_attn(**a)
+
+
+# ---------------------------------------------------------------------------------------
+# P1: independent brute force
+# ---------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("case", _tiny_cases(), ids=lambda c: f"R{c.R}T{c.T}H{c.Hkv}{'n' if c.qknorm else 'p'}")
+def test_bruteforce_tiny(case):
+    ref = bruteforce(**case.np_args(), qknorm=case.qknorm)
+    assert _rel(_oracle(case), ref) <= TOL
+
+
+@pytest.mark.parametrize("n", [1, 2, 3])
+def test_bruteforce_configs(n):
+    case = ds.make_config(n)
+    ref = bruteforce(**case.np_args(), qknorm=case.qknorm)
+    assert _rel(_oracle(case), ref) <= TOL
+
+
+def test_bruteforce_block_lens():
+    case = ds.make_case(3, 5, 12, 2, [70, 0, 129], seed=5, block_lens=[2, 5, 1], qknorm=True,
+                        pool_pages=8)
+    out = _oracle(case)
+    assert _rel(out, bruteforce(**case.np_args(), qknorm=True)) <= TOL
+    # rows past a block length are zero
+    assert np.all(out[2:5] == 0) and np.all(out[11:15] == 0)
+
+
+# ---------------------------------------------------------------------------------------
+# P2: library routine (torch float64 SDPA on gathered dense tensors, GQA expanded)
+# ---------------------------------------------------------------------------------------
+
+def _sdpa_reference(case):
+    a = case.np_args()
+    Hq, Hkv, T, D = case.Hq, case.Hkv, case.T, 64
+    qkv = torch.from_numpy(a["qkv"])
+    kp, vp = torch.from_numpy(a["k_pool"]), torch.from_numpy(a["v_pool"])
+    out = torch.zeros(case.R * T, Hq * D, dtype=torch.float64)
+    for r in range(case.R):
+        L = int(a["context_lens"][r])
+        idx = torch.arange(L)
+        pages = torch.from_numpy(a["page_table"][r])[idx // 64] if L else idx
+        rows = qkv[r * T:(r + 1) * T]
+        q = rows[:, :Hq * D].reshape(T, Hq, D).transpose(0, 1)             # [Hq, T, D]
+        kb = rows[:, Hq * D:(Hq + Hkv) * D].reshape(T, Hkv, D).transpose(0, 1)
+        vb = rows[:, (Hq + Hkv) * D:(Hq + 2 * Hkv) * D].reshape(T, Hkv, D).transpose(0, 1)
+        kc = kp[pages, :, idx % 64, :].transpose(0, 1)                      # [Hkv, L, D]
+        vc = vp[pages, :, idx % 64, :].transpose(0, 1)
+        k = torch.cat([kc, kb], 1).repeat_interleave(6, 0)
+        v = torch.cat([vc, vb], 1).repeat_interleave(6, 0)
+        o = torch.nn.functional.scaled_dot_product_attention(
+            q.unsqueeze(0), k.unsqueeze(0), v.unsqueeze(0), scale=case.scale)[0]
+        out[r * T:(r + 1) * T] = o.transpose(0, 1).reshape(T, Hq * D)
+    return out.numpy()
+
+
+@pytest.mark.parametrize("n", [1, 2, 3])
+def test_sdpa_plain(n):
+    case = ds.make_config(n)
+    case.qknorm = False  # plain path on the same tensors
+    assert _rel(oracle.drafter_attn(**case.np_args()), _sdpa_reference(case)) <= TOL
+
+
+def test_sdpa_decode_special_case():
+    # T=1, Hkv=1: ordinary single-query paged decode attention
+    case = ds.make_case(4, 1, 6, 1, [1, 64, 700, 2041], seed=3, pool_pages=60)
+    assert _rel(oracle.drafter_attn(**case.np_args()), _sdpa_reference(case)) <= TOL
+
+
+# ---------------------------------------------------------------------------------------
+# P3: split-merge algebra; P4 / I1: weights sum to one
+# ---------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("S", [1, 2, 3, 7, 32])
+def test_split_merge_equals_definition(S):
+    case = ds.make_config(2)
+    ref = _oracle(case)
+    got = oracle.drafter_attn_split_merge(**case.np_args(), num_splits=S, qknorm=True)
+    assert _rel(got, ref) <= 1e-13
+
+
+def test_softmax_weights_sum_to_one():
+    case = ds.make_config(3)
+    _, probs = _oracle(case, return_probs=True)
+    L = case.context_lens.tolist()
+    for (r, h, t), p in probs.items():
+        assert abs(p.sum() - 1.0) <= 1e-13
+        assert p.shape[0] == L[r] + case.T
+        assert np.all(p >= 0)
+
+
+# ---------------------------------------------------------------------------------------
+# closed forms
+# ---------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("qk", [False, True])
+def test_empty_context_single_token_returns_v(qk):
+    # P5: one key, weight one -> the output is the block's own v (never normalised)
+    case = ds.make_case(3, 1, 24, 4, [0, 0, 0], seed=9, stride=0, qknorm=qk)
+    out = _oracle(case)
+    qkv = case.np_args()["qkv"]
+    for h in range(24):
+        g = h // 6
+        np.testing.assert_array_equal(out[:, h * 64:(h + 1) * 64], qkv[:, (24 + 4 + g) * 64:(24 + 4 + g + 1) * 64])
+
+
+@pytest.mark.parametrize("qk", [False, True])
+def test_zero_query_gives_uniform_mean(qk):
+    # P6: q = 0 -> all scores 0 -> plain mean of the L + T values (rms(0)=0, rope(0)=0)
+    case = ds.make_case(2, 3, 6, 1, [100, 5], seed=21, qknorm=qk)
+    case.qkv[:, :6 * 64] = 0
+    a = case.np_args()
+    out = _oracle(case)
+    for r in range(2):
+        L = int(a["context_lens"][r])
+        kc, vc = oracle.gather_context(a["k_pool"], a["v_pool"], a["page_table"][r], L, 0)
+        vals = np.concatenate([vc, a["qkv"][r * 3:(r + 1) * 3, 7 * 64:8 * 64]])
+        mean = vals.sum(0) / (L + 3)
+        for t in range(3):
+            for h in range(6):
+                np.testing.assert_allclose(out[r * 3 + t, h * 64:(h + 1) * 64], mean, rtol=0, atol=1e-14)
+
+
+def test_gathered_context_matches_direct_indexing():
+    case = ds.make_config(2)
+    a = case.np_args()
+    for r in range(8):
+        L = int(a["context_lens"][r])
+        kc, vc = oracle.gather_context(a["k_pool"], a["v_pool"], a["page_table"][r], L, 0)
+        for c in [0, L // 2, L - 1] if L else []:
+            p = a["page_table"][r][c // 64]
+            np.testing.assert_array_equal(kc[c], a["k_pool"][p, 0, c % 64])
+            np.testing.assert_array_equal(vc[c], a["v_pool"][p, 0, c % 64])
+
+
+@pytest.mark.parametrize("qk", [False, True])
+def test_constant_v_gives_constant(qk):
+    # P7: every value row equal to c -> output c whatever the keys are
+    case = ds.make_case(2, 4, 12, 2, [130, 64], seed=4, qknorm=qk, pool_pages=4)
+    c = torch.linspace(-2, 2, 64).to(torch.bfloat16)
+    case.qkv[:, (12 + 2) * 64:] = c.repeat(2)
+    case.pool[:, 1] = c
+    out = _oracle(case)
+    for h in range(12):
+        np.testing.assert_allclose(out[:, h * 64:(h + 1) * 64], np.tile(c.double().numpy(), (8, 1)),
+                                   rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("where", ["first", "last_page", "tail_slot", "block"])
+def test_needle(where):
+    # P8: one key aligned with q and scaled up, its value e_m -> the output is e_m
+    R, T = 2, 2
+    case = ds.make_case(R, T, 6, 1, [200, 130], seed=31, pool_pages=8)
+    a = case.np_args()
+    r, t, h, m = 1, 1, 3, 17
+    L = 130
+    j = {"first": 0, "last_page": 64 + 5, "tail_slot": L - 1, "block": L + 1}[where]
+    q = np.zeros(64)
+    q[5] = 1.0
+    case.qkv[r * T + t, h * 64:(h + 1) * 64] = torch.from_numpy(q).to(torch.bfloat16)
+    e = torch.zeros(64)
+    e[m] = 1.0
+    if j < L:
+        p = int(a["page_table"][r][j // 64])
+        case.k_pool[p, 0, j % 64] = torch.from_numpy(2000.0 * q).to(torch.bfloat16)
+        case.v_pool[p, 0, j % 64] = e.to(torch.bfloat16)
+    else:
+        row = r * T + (j - L)
+        case.qkv[row, 6 * 64:7 * 64] = torch.from_numpy(2000.0 * q).to(torch.bfloat16)
+        case.qkv[row, 7 * 64:8 * 64] = e.to(torch.bfloat16)
+    out = _oracle(case)
+    np.testing.assert_allclose(out[r * T + t, h * 64:(h + 1) * 64], e.double().numpy(), atol=1e-12)
+
+
+def test_rmsnorm_closed_forms():
+    w = np.linspace(0.5, 1.5, 64)
+    for c in (1e-3, 0.5, 3.0, -7.0):
+        x = np.full(64, c)
+        np.testing.assert_allclose(oracle.rms_norm(x, w, 1e-5), w * c / math.sqrt(c * c + 1e-5), rtol=1e-15)
+    # scale invariance for |alpha x| >> sqrt(eps)
+    x = np.random.default_rng(0).standard_normal(64)
+    np.testing.assert_allclose(oracle.rms_norm(1e3 * x, w, 1e-5), oracle.rms_norm(x, w, 1e-5), rtol=1e-5)
+    # unit weight and unit-mean-square input -> unchanged up to eps
+    y = np.sign(x)
+    np.testing.assert_allclose(oracle.rms_norm(y, np.ones(64), 0.0), y, rtol=1e-15)
+
+
+def test_rope_closed_forms():
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((5, 64))
+    # pos 0 is the identity
+    np.testing.assert_array_equal(oracle.rope_neox(x, np.zeros(5), 10000.0), x)
+    # e_i at position p lands on (cos, sin) of p * f_i in dims (i, i+32); exact decimal
+    # frequencies at i = 0, 8, 16, 24: 10000**(-2i/64) = 1, 0.1, 0.01, 0.001
+    for i, f in [(0, 1.0), (8, 0.1), (16, 0.01), (24, 0.001)]:
+        for p in (1, 7, 2041, 32775):
+            e = np.zeros(64)
+            e[i] = 1.0
+            y = oracle.rope_neox(e, np.array(p), 10000.0)
+            assert abs(y[i] - math.cos(p * f)) < 1e-12 and abs(y[i + 32] - math.sin(p * f)) < 1e-12
+            assert np.count_nonzero(np.abs(y) > 1e-15) <= 2
+            e2 = np.zeros(64)
+            e2[i + 32] = 1.0
+            y2 = oracle.rope_neox(e2, np.array(p), 10000.0)
+            assert abs(y2[i] + math.sin(p * f)) < 1e-12 and abs(y2[i + 32] - math.cos(p * f)) < 1e-12
+    # each (i, i+32) pair keeps its length
+    y = oracle.rope_neox(x, np.arange(5) * 977, 10000.0)
+    np.testing.assert_allclose(np.hypot(y[:, :32], y[:, 32:]), np.hypot(x[:, :32], x[:, 32:]), rtol=1e-13)
+
+
+def test_rope_relative_position_property():
+    # with no context, scores depend only on position differences: shift all positions
+    case = ds.make_case(2, 6, 12, 2, [0, 0], seed=8, stride=0, qknorm=True)
+    a = case.np_args()
+    base = oracle.drafter_attn_qknorm(**a)
+    a["positions"] = a["positions"] + 12345
+    np.testing.assert_allclose(oracle.drafter_attn_qknorm(**a), base, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------------------
+# invariants
+# ---------------------------------------------------------------------------------------
+
+def test_qknorm_equals_explicit_norm_rope_then_attention():
+    # I7: the qknorm variant == plain attention on explicitly normalised+rotated q and k
+    case = ds.make_config(3)
+    a = case.np_args()
+    ref = oracle.drafter_attn_qknorm(**a)
+    qkv = a["qkv"].copy()
+    T, Hq, Hkv = case.T, case.Hq, case.Hkv
+    pos = a["positions"]
+    for h in range(Hq):
+        qkv[:, h * 64:(h + 1) * 64] = oracle.rope_neox(oracle.rms_norm(qkv[:, h * 64:(h + 1) * 64], a["q_norm_weight"], 1e-5), pos, 1e4)
+    for g in range(Hkv):
+        c = slice((Hq + g) * 64, (Hq + g + 1) * 64)
+        qkv[:, c] = oracle.rope_neox(oracle.rms_norm(qkv[:, c], a["k_norm_weight"], 1e-5), pos, 1e4)
+    a["qkv"] = qkv
+    np.testing.assert_array_equal(oracle.drafter_attn(**a), ref)
+
+
+def test_page_permutation_invariance():
+    # I2: moving pages to other physical slots (and the table with them) changes nothing
+    case = ds.make_config(2)
+    a = case.np_args()
+    ref = oracle.drafter_attn_qknorm(**a)
+    P = a["k_pool"].shape[0]
+    perm = np.random.default_rng(5).permutation(P)
+    inv = np.argsort(perm)
+    a2 = dict(a)
+    a2["k_pool"] = a["k_pool"][perm]
+    a2["v_pool"] = a["v_pool"][perm]
+    a2["page_table"] = inv[a["page_table"]]
+    np.testing.assert_array_equal(oracle.drafter_attn_qknorm(**a2), ref)
+
+
+def test_request_isolation():
+    # I4: another request's rows, pages and length do not move this request's output
+    case = ds.make_config(3)
+    a = case.np_args()
+    ref = oracle.drafter_attn_qknorm(**a)
+    a2 = {k: (v.copy() if isinstance(v, np.ndarray) else v) for k, v in a.items()}
+    k = 2
+    a2["qkv"][k * 8:(k + 1) * 8] += 1.0
+    L = int(a2["context_lens"][k])
+    for p in a2["page_table"][k][: -(-L // 64)]:
+        a2["k_pool"][p] *= -1
+    a2["context_lens"][k] = max(0, L - 37)
+    got = oracle.drafter_attn_qknorm(**a2)
+    keep = np.ones(64, bool)
+    keep[k * 8:(k + 1) * 8] = False
+    np.testing.assert_array_equal(got[keep], ref[keep])
+    assert not np.array_equal(got[~keep], ref[~keep])
+
+
+def test_empty_context_attends_to_own_block_only():
+    # I3: L = 0 -> softmax over the block's own keys only
+    case = ds.make_case(2, 5, 6, 1, [0, 0], seed=12, stride=2, pool_pages=3)
+    a = case.np_args()
+    out = oracle.drafter_attn(**a)
+    qkv = a["qkv"]
+    for r in range(2):
+        rows = qkv[r * 5:(r + 1) * 5]
+        q = torch.from_numpy(rows[:, :6 * 64].reshape(5, 6, 64).transpose(1, 0, 2).copy())
+        k = torch.from_numpy(rows[:, 6 * 64:7 * 64].copy()).expand(6, 5, 64)
+        v = torch.from_numpy(rows[:, 7 * 64:8 * 64].copy()).expand(6, 5, 64)
+        o = torch.nn.functional.scaled_dot_product_attention(q, k, v, scale=0.125)
+        np.testing.assert_allclose(out[r * 5:(r + 1) * 5], o.transpose(0, 1).reshape(5, 384).numpy(), atol=1e-13)
+
+
+def test_poison_does_not_change_result():
+    # I6: NaN in unreferenced pages / tail slots / row padding and garbage table entries
+    clean = ds.make_config(2)
+    dirty = ds.make_config(2, poison=True)
+    np.testing.assert_array_equal(_oracle(dirty), _oracle(clean))
+    assert not np.isnan(_oracle(dirty)).any()
+
+
+def test_oracle_rejects_out_of_contract():
+    case = ds.make_config(2)
+    a = case.np_args()
+    bad = dict(a)
+    bad["context_lens"] = a["context_lens"].copy()
+    bad["context_lens"][0] = 32 * 64 + 1
+    with pytest.raises(oracle.OracleContractError):
+        oracle.drafter_attn_qknorm(**bad)
+    bad = dict(a)
+    bad["page_table"] = a["page_table"].copy()
+    r = int(np.argmax(a["context_lens"]))
+    bad["page_table"][r, 0] = 10_000
+    with pytest.raises(oracle.OracleContractError):
+        oracle.drafter_attn_qknorm(**bad)
+    with pytest.raises(oracle.OracleContractError):
+        oracle.drafter_attn(**dict(a, num_q_heads=12))
