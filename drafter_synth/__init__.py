@@ -78,11 +78,13 @@ class DrafterCase:
         return int(L.sum()) * self.Hkv * HEAD_DIM * 2 * 2
 
     # ---- float64 numpy views for the oracle (values are exact bf16 values) ----
-    def np_args(self) -> dict:
+    def np_args(self, pools=None) -> dict:
+        """Oracle arguments; ``pools=(k, v)`` passes already converted float64 pools."""
         f = lambda t: None if t is None else t.to(torch.float64).numpy()
         i = lambda t: None if t is None else t.to(torch.int64).numpy()
+        kp, vp = pools if pools is not None else (f(self.k_pool), f(self.v_pool))
         return dict(
-            qkv=f(self.qkv), k_pool=f(self.k_pool), v_pool=f(self.v_pool),
+            qkv=f(self.qkv), k_pool=kp, v_pool=vp,
             page_table=i(self.page_table), context_lens=i(self.context_lens),
             block_lens=i(self.block_lens), positions=i(self.positions),
             q_norm_weight=f(self.q_norm_weight), k_norm_weight=f(self.k_norm_weight),
@@ -115,7 +117,8 @@ def make_case(R: int, T: int, Hq: int, Hkv: int, lens: Sequence[int], *,
               block_lens: Optional[Sequence[int]] = None, poison: bool = False,
               separate_pools: bool = False, qkv_row_pad: int = 0,
               scale: Optional[float] = None, v_mean: float = 0.0,
-              pos_offset: Optional[Sequence[int]] = None, name: str = "") -> DrafterCase:
+              pos_offset: Optional[Sequence[int]] = None, name: str = "",
+              pool_override: Optional[torch.Tensor] = None) -> DrafterCase:
     """Draw one case.
 
     q/k/v and pool values ~ N(0,1) (V ~ N(v_mean, 1)), rounded to bf16.
@@ -123,7 +126,8 @@ def make_case(R: int, T: int, Hq: int, Hkv: int, lens: Sequence[int], *,
     ``poison=True`` fills every pool element the definition never reads
     (unreferenced pages, slots past the context length in the last page),
     the qkv row padding and rows past a block length with NaN, and the unused
-    page-table entries with 0x7FFFFFFF.
+    page-table entries with 0x7FFFFFFF.  ``pool_override`` reuses an existing
+    ``[P, 2, Hkv, 64, 64]`` bf16 pool instead of drawing one (no poison then).
     """
     assert len(lens) == R
     rng = np.random.default_rng(seed)
@@ -141,8 +145,12 @@ def make_case(R: int, T: int, Hq: int, Hkv: int, lens: Sequence[int], *,
     qkv = rng.standard_normal((R * T, width + qkv_row_pad), dtype=np.float32)
     vcol = slice((Hq + Hkv) * D, width)
     qkv[:, vcol] += v_mean
-    pool = rng.standard_normal((pool_pages, 2, Hkv, PAGE, D), dtype=np.float32)
-    pool[:, 1] += v_mean
+    if pool_override is not None:
+        assert not poison and tuple(pool_override.shape) == (pool_pages, 2, Hkv, PAGE, D)
+        pool = None
+    else:
+        pool = rng.standard_normal((pool_pages, 2, Hkv, PAGE, D), dtype=np.float32)
+        pool[:, 1] += v_mean
 
     perm = rng.permutation(pool_pages)
     wq = rng.uniform(0.5, 1.5, size=D)
@@ -182,7 +190,7 @@ def make_case(R: int, T: int, Hq: int, Hkv: int, lens: Sequence[int], *,
                 qkv[r * T + bl[r]:(r + 1) * T, :] = np.nan
 
     qkv_t = _bf16(qkv)
-    pool_t = _bf16(pool)
+    pool_t = pool_override if pool_override is not None else _bf16(pool)
     if separate_pools:
         k_pool = pool_t[:, 0].contiguous()
         v_pool = pool_t[:, 1].contiguous()
@@ -240,7 +248,14 @@ def config3(k: int = 0, poison: bool = False) -> DrafterCase:
                      pos_dtype=torch.int64, poison=poison, name="cfg3")
 
 
-def config4_cell(r: int, t: int, hkv: int, k: int = 0, poison: bool = False) -> DrafterCase:
+def config4_pool(hkv: int) -> torch.Tensor:
+    """The 512-page pool shared by every cell of one head layout in the split sweep."""
+    rng = np.random.default_rng(1000 * 4 + hkv)
+    return _bf16(rng.standard_normal((512, 2, hkv, PAGE, HEAD_DIM), dtype=np.float32))
+
+
+def config4_cell(r: int, t: int, hkv: int, k: int = 0, poison: bool = False,
+                 pool: Optional[torch.Tensor] = None) -> DrafterCase:
     """One cell of the split sweep: r requests x t tokens, 6/1 (hkv=1) or 24/4 (hkv=4),
     qknorm, L ~ U{0..2041}, dense rows of stride 32 in a 512-page pool; int32
     positions for 6/1, int64 for 24/4.  ``k`` indexes the redraw (replay)."""
@@ -249,7 +264,7 @@ def config4_cell(r: int, t: int, hkv: int, k: int = 0, poison: bool = False) -> 
     seed = int(rng.integers(1 << 31))
     return make_case(r, t, 6 * hkv, hkv, lens, seed=seed, stride=32, pool_pages=512,
                      qknorm=True, pos_dtype=torch.int32 if hkv == 1 else torch.int64,
-                     poison=poison, name=f"cfg4_r{r}t{t}h{hkv}_{k}")
+                     poison=poison, name=f"cfg4_r{r}t{t}h{hkv}_{k}", pool_override=pool)
 
 
 def config5(k: int = 0, poison: bool = False) -> DrafterCase:

@@ -1,0 +1,171 @@
+/*
+ * drafter_attn.h -- C ABI of the MI355X (gfx950) drafter block-attention library.
+ *
+ * The operation (TensorRT-LLM PR #20532 "Share Kimi K3 FP4 modeling and add NVFP4
+ * support on SM103", Conversation: the commit that adds k3_drafter_attn and
+ * k3_drafter_attn_qknorm, and the next commit that adds their contracts):
+ *
+ *   Each of up to 8 requests brings a draft block of up to 8 tokens.  Every
+ *   block attends densely (no causal mask) to its request's paged context and
+ *   to its own K/V, which are read from the packed qkv rows and are never
+ *   written into the page pool.  GQA with 6 query heads per KV head, head_dim
+ *   64, HND pages of 64 tokens.  Head layouts 6/1 and 24/4; context lengths 0
+ *   to 2041 in the contract tests; page tables as dense or strided rows with
+ *   padded page strides; int32 or int64 positions.  drafter_attn takes q/k that
+ *   are already normalised and rotated; drafter_attn_qknorm applies the
+ *   per-head q/k RMSNorm (eps 1e-5) and the NeoX rotary embedding (base 10000)
+ *   inside the kernel.  Lengths, page tables and qkv are read on the device,
+ *   so a call captured in a HIP graph replays correctly after those buffers
+ *   are rewritten in place.
+ *
+ * For request r, block token t < b_r, query head h (KV head g = h / 6):
+ *
+ *   out[r*T+t, h*64:(h+1)*64] = sum_j softmax_j(scale * <q, key_j>) * value_j
+ *
+ * over the L_r context tokens (token c: slot c%64 of page page_table[r][c/64])
+ * followed by the b_r block tokens (k and v heads g of qkv rows r*T .. r*T+b_r-1).
+ * In the qknorm variant q and the block's k are first replaced by
+ * rope(rmsnorm(x, w), position); context K/V and every v are used as stored.
+ *
+ * Layouts (bf16 = IEEE bfloat16 bit patterns, little endian):
+ *   qkv        [R*T rows][qkv_row_stride elements]; row r*T+t holds q heads
+ *              0..Hq-1, then k heads 0..Hkv-1, then v heads 0..Hkv-1, 64 each.
+ *   k_pool     page p at k_pool + p*pool_page_stride elements, laid out
+ *              [Hkv][64 slots][64 dims] (HND).  v_pool likewise, same stride
+ *              (a fused [P][2][Hkv][64][64] pool is v_pool = k_pool + Hkv*4096,
+ *              pool_page_stride = 2*Hkv*4096).
+ *   page_table int32 [R][page_table_stride]; only the first ceil(L_r/64)
+ *              entries of row r are read.  Other entries may hold anything.
+ *   out        [R*T rows][out_row_stride elements] bf16; rows t >= b_r are
+ *              written as zeros.
+ *   positions  int32 or int64 [R*T], read per token (row order of qkv).
+ *
+ * Pointers: every array argument is a DEVICE pointer owned by the caller, except
+ * that `stream` is a hipStream_t (NULL = the null stream).  The library
+ * allocates nothing and never synchronises the host with the device: calls are
+ * asynchronous in `stream` order and may be captured into a HIP graph.
+ * Only `out`, `workspace` and `status_word` are written; qkv, the pools and the
+ * page table are left bit-identical.
+ *
+ * Errors: every shape, stride, alignment, aliasing and workspace check runs on
+ * the host before any launch and returns a negative da_status with a message
+ * retrievable through drafter_attn_last_error() (thread-local).  Values that
+ * live on the device (lengths, page ids, block lengths) cannot be checked
+ * without a synchronisation: the kernel clamps them into range so that it never
+ * reads outside the arrays described above, and ORs a DA_FLAG_* bit into
+ * *status_word when one was out of contract (status_word may be NULL).
+ */
+#ifndef DRAFTER_ATTN_H
+#define DRAFTER_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum da_status {
+  DA_OK = 0,
+  DA_EINVAL = -1,        /* an argument is outside the contract */
+  DA_EUNSUPPORTED = -2,  /* head_dim / page_size / GQA ratio other than 64 / 64 / 6 */
+  DA_EWORKSPACE = -3,    /* workspace missing or smaller than drafter_attn_workspace_bytes() */
+  DA_ELAUNCH = -4        /* the HIP runtime refused the launch (no device, bad stream, ...) */
+} da_status;
+
+enum { DA_POS_INT32 = 0, DA_POS_INT64 = 1 };
+
+/* Bits ORed into *status_word by the kernel. */
+enum {
+  DA_FLAG_CONTEXT_LEN = 1, /* some L_r < 0 or > page_table_stride*64 (clamped) */
+  DA_FLAG_PAGE_ID = 2,     /* some referenced page id outside [0, num_pages) (clamped) */
+  DA_FLAG_BLOCK_LEN = 4    /* some b_r outside [1, T] (clamped) */
+};
+
+/* Hard limits of the contract. */
+#define DA_MAX_REQUESTS 8
+#define DA_MAX_TOKENS 8
+#define DA_MAX_KV_HEADS 16
+#define DA_HEAD_DIM 64
+#define DA_PAGE_SIZE 64
+#define DA_GQA 6
+
+/*
+ * Bytes of workspace a call with these sizes needs (0 for arguments outside the
+ * contract).  The workspace holds one fp32 partial (running max, weight sum,
+ * unnormalised output) per (request, KV head, context split) and one counter
+ * per (request, KV head).  The counters must be zero before the first call on
+ * a workspace (zero the whole buffer once after allocating it); every call
+ * leaves them zero again.  Two calls in flight on one workspace race.
+ */
+size_t drafter_attn_workspace_bytes(int32_t num_requests, int32_t tokens_per_block,
+                                    int32_t num_q_heads, int32_t num_kv_heads,
+                                    int32_t page_table_stride);
+
+/*
+ * The split-KV plan the library uses for these sizes: the page-table row is cut
+ * into *num_splits ranges of *pages_per_split pages, each processed by one
+ * workgroup.  It depends only on these host values (never on device data), so
+ * results are bit-identical across reruns and graph replays.  Returns DA_OK or
+ * DA_EINVAL.
+ */
+int drafter_attn_plan(int32_t num_requests, int32_t num_kv_heads, int32_t page_table_stride,
+                      int32_t* num_splits, int32_t* pages_per_split);
+
+/*
+ * k3_drafter_attn: q and the block's k are used as given (already normalised and
+ * rotated).  scale must be finite and > 0 (usually 1/sqrt(64)).
+ * Alignment: qkv, k_pool, v_pool and out 16-byte aligned; qkv_row_stride,
+ * out_row_stride and pool_page_stride multiples of 8 elements.
+ * out must not overlap any input or the workspace.
+ */
+int drafter_attn(const void* qkv, int64_t qkv_row_stride,
+                 const void* k_pool, const void* v_pool, int64_t pool_page_stride,
+                 int32_t num_pages,
+                 const int32_t* page_table, int32_t page_table_stride,
+                 const int32_t* context_lens, const int32_t* block_lens /* NULL = all T */,
+                 int32_t num_requests, int32_t tokens_per_block,
+                 int32_t num_q_heads, int32_t num_kv_heads,
+                 int32_t head_dim, int32_t page_size,
+                 float scale,
+                 void* workspace, size_t workspace_bytes,
+                 void* out, int64_t out_row_stride,
+                 int32_t* status_word /* NULL = off */,
+                 void* stream /* hipStream_t */);
+
+/*
+ * k3_drafter_attn_qknorm: as drafter_attn, but q and the block's k are first
+ * normalised, x * w / sqrt(mean(x^2) + eps) over each head's 64 values (q heads
+ * use q_norm_weight, k heads k_norm_weight; bf16 [64] each), then rotated NeoX
+ * style: dims i and i+32 (i < 32) turn by pos * rope_base^(-2i/64) with pos =
+ * positions[r*T+t].  The block's v and the paged context are not touched.
+ * eps must be finite and >= 0, rope_base finite and > 0; positions_dtype is
+ * DA_POS_INT32 or DA_POS_INT64.  The angle is formed and reduced in fp64, the
+ * rotation and the norm are computed in fp32, and q/k are rounded to bf16 once
+ * before the contractions.
+ */
+int drafter_attn_qknorm(const void* qkv, int64_t qkv_row_stride,
+                        const void* k_pool, const void* v_pool, int64_t pool_page_stride,
+                        int32_t num_pages,
+                        const int32_t* page_table, int32_t page_table_stride,
+                        const int32_t* context_lens, const int32_t* block_lens,
+                        int32_t num_requests, int32_t tokens_per_block,
+                        int32_t num_q_heads, int32_t num_kv_heads,
+                        int32_t head_dim, int32_t page_size,
+                        float scale,
+                        const void* positions, int32_t positions_dtype,
+                        const void* q_norm_weight, const void* k_norm_weight,
+                        float eps, float rope_base,
+                        void* workspace, size_t workspace_bytes,
+                        void* out, int64_t out_row_stride,
+                        int32_t* status_word,
+                        void* stream);
+
+/* Message for the last non-DA_OK return on this thread ("" if none). */
+const char* drafter_attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DRAFTER_ATTN_H */

@@ -1,0 +1,47 @@
+"""Ahead-of-time build of the gfx950 HIP library ``libdrafter_attn.so`` (in-tree).
+
+Usage: ``python -m speculative_decoding_drafter_amd.build`` or ``build_library()``.
+"""
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+SRC = os.path.join(PKG, "csrc", "drafter_attn.hip")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libdrafter_attn.so")
+ARCH = "gfx950"
+
+# -packed-fp32-ops: keep the compiler from forming v_pk_{add,mul,fma}_f32
+HIPCC_FLAGS = [
+    "-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build the HIP library)")
+
+
+def build_library(verbose: bool = False) -> str:
+    """Compile the library from source (always) and return the path of the .so."""
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-o", tmp, SRC]
+    res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    msgs = [ln for ln in res.stdout.splitlines() if "packed-fp32-ops" not in ln]
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + "\n".join(msgs))
+    if verbose and msgs:
+        print("\n".join(msgs), file=sys.stderr)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build_library(verbose=True))

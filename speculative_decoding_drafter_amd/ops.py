@@ -1,0 +1,166 @@
+"""torch binding of the drafter block-attention C ABI (argument marshalling only).
+
+Every step of the computation runs in the HIP library; torch provides device
+memory and the current stream.  Shape, dtype and device problems raise
+``DrafterAttnError`` (a ``ValueError``) before anything is launched, as do the
+library's own host-side checks.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib
+
+HEAD_DIM = 64
+PAGE = 64
+GQA = 6
+POS_DTYPES = {torch.int32: 0, torch.int64: 1}
+
+
+class DrafterAttnError(ValueError):
+    """An argument outside the operation's contract."""
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def workspace_bytes(num_requests: int, tokens_per_block: int, num_q_heads: int, num_kv_heads: int,
+                    page_table_stride: int) -> int:
+    n = _lib.load().drafter_attn_workspace_bytes(num_requests, tokens_per_block, num_q_heads,
+                                                 num_kv_heads, page_table_stride)
+    if n == 0:
+        raise DrafterAttnError("sizes outside the contract")
+    return int(n)
+
+
+def plan(num_requests: int, num_kv_heads: int, page_table_stride: int) -> Tuple[int, int]:
+    """(num_splits, pages_per_split) the library uses for these sizes."""
+    s, p = ctypes.c_int32(), ctypes.c_int32()
+    rc = _lib.load().drafter_attn_plan(num_requests, num_kv_heads, page_table_stride,
+                                       ctypes.byref(s), ctypes.byref(p))
+    if rc != 0:
+        raise DrafterAttnError(_lib.last_error())
+    return s.value, p.value
+
+
+def make_workspace(num_requests: int, tokens_per_block: int, num_q_heads: int, num_kv_heads: int,
+                   page_table_stride: int, device) -> torch.Tensor:
+    """A zeroed workspace (its counters must start at zero; every call leaves them zero)."""
+    n = workspace_bytes(num_requests, tokens_per_block, num_q_heads, num_kv_heads, page_table_stride)
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def _check(cond: bool, msg: str):
+    if not cond:
+        raise DrafterAttnError(msg)
+
+
+def _common(qkv, k_pool, v_pool, page_table, context_lens, block_lens, num_q_heads, num_kv_heads,
+            tokens_per_block, out, workspace):
+    dev = qkv.device
+    _check(dev.type == "cuda", "qkv must be a GPU tensor (there is no CPU path)")
+    R = int(context_lens.shape[0]) if context_lens.dim() == 1 else -1
+    T = int(tokens_per_block)
+    Hq, Hkv = int(num_q_heads), int(num_kv_heads)
+    _check(context_lens.dim() == 1 and context_lens.dtype == torch.int32, "context_lens must be int32 [R]")
+    _check(qkv.dtype == torch.bfloat16 and qkv.dim() == 2 and qkv.stride(1) == 1,
+           "qkv must be bf16 [R*T, row_stride] with unit column stride")
+    _check(qkv.shape[0] == R * T, f"qkv has {qkv.shape[0]} rows, expected R*T = {R * T}")
+    _check(qkv.shape[1] >= (Hq + 2 * Hkv) * HEAD_DIM, "qkv is narrower than (Hq + 2*Hkv) * 64")
+    _check(page_table.dtype == torch.int32 and page_table.dim() == 2 and page_table.shape[0] == R,
+           "page_table must be int32 [R, stride]")
+    stride = int(page_table.shape[1])
+    _check(stride == 0 or (page_table.stride(1) == 1 and page_table.stride(0) == stride),
+           "page_table must be contiguous")
+    for name, pool in (("k_pool", k_pool), ("v_pool", v_pool)):
+        _check(pool.dtype == torch.bfloat16 and pool.dim() == 4, f"{name} must be bf16 [P, Hkv, 64, 64]")
+        _check(tuple(pool.shape[1:]) == (Hkv, PAGE, HEAD_DIM), f"{name} must be [P, {Hkv}, 64, 64]")
+        _check(pool.stride()[1:] == (PAGE * HEAD_DIM, HEAD_DIM, 1), f"{name} pages must be contiguous HND")
+        _check(pool.device == dev, f"{name} must be on {dev}")
+    _check(k_pool.shape[0] == v_pool.shape[0] and k_pool.stride(0) == v_pool.stride(0),
+           "k_pool and v_pool must have the same page count and page stride")
+    for name, t in (("page_table", page_table), ("context_lens", context_lens), ("block_lens", block_lens),
+                    ("out", out), ("workspace", workspace)):
+        if t is not None:
+            _check(t.device == dev, f"{name} must be on {dev}")
+    if block_lens is not None:
+        _check(block_lens.dtype == torch.int32 and tuple(block_lens.shape) == (R,), "block_lens must be int32 [R]")
+        _check(block_lens.is_contiguous(), "block_lens must be contiguous")
+    _check(context_lens.is_contiguous(), "context_lens must be contiguous")
+    if out is None:
+        out = torch.empty(R * T, Hq * HEAD_DIM, dtype=torch.bfloat16, device=dev)
+    _check(out.dtype == torch.bfloat16 and out.dim() == 2 and out.stride(1) == 1 and
+           out.shape[0] == R * T and out.shape[1] >= Hq * HEAD_DIM, "out must be bf16 [R*T, >= Hq*64]")
+    if workspace is None:
+        workspace = make_workspace(R, T, Hq, Hkv, stride, dev)
+    _check(workspace.is_contiguous(), "workspace must be contiguous")
+    return dict(R=R, T=T, Hq=Hq, Hkv=Hkv, stride=stride, out=out, workspace=workspace, dev=dev)
+
+
+def _stream(dev) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _raise(rc: int):
+    if rc != 0:
+        raise DrafterAttnError(f"drafter_attn error {rc}: {_lib.last_error()}")
+
+
+def drafter_attn(qkv: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, page_table: torch.Tensor,
+                 context_lens: torch.Tensor, *, num_q_heads: int, num_kv_heads: int, tokens_per_block: int,
+                 block_lens: Optional[torch.Tensor] = None, scale: Optional[float] = None,
+                 out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                 status: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """k3_drafter_attn (q/k already normalised and rotated).  Returns ``out`` [R*T, Hq*64] bf16."""
+    lib = _lib.load()
+    a = _common(qkv, k_pool, v_pool, page_table, context_lens, block_lens, num_q_heads, num_kv_heads,
+                tokens_per_block, out, workspace)
+    scale = 1.0 / math.sqrt(HEAD_DIM) if scale is None else float(scale)
+    if status is not None:
+        _check(status.dtype == torch.int32 and status.numel() >= 1 and status.device == a["dev"],
+               "status must be an int32 GPU tensor")
+    rc = lib.drafter_attn(
+        qkv.data_ptr(), qkv.stride(0), k_pool.data_ptr(), v_pool.data_ptr(), k_pool.stride(0), k_pool.shape[0],
+        _ptr(page_table) if a["stride"] else None, a["stride"], context_lens.data_ptr(), _ptr(block_lens),
+        a["R"], a["T"], a["Hq"], a["Hkv"], HEAD_DIM, PAGE, scale,
+        a["workspace"].data_ptr(), a["workspace"].numel(), a["out"].data_ptr(), a["out"].stride(0),
+        _ptr(status), _stream(a["dev"]))
+    _raise(rc)
+    return a["out"]
+
+
+def drafter_attn_qknorm(qkv: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, page_table: torch.Tensor,
+                        context_lens: torch.Tensor, positions: torch.Tensor, q_norm_weight: torch.Tensor,
+                        k_norm_weight: torch.Tensor, *, num_q_heads: int, num_kv_heads: int,
+                        tokens_per_block: int, block_lens: Optional[torch.Tensor] = None,
+                        scale: Optional[float] = None, eps: float = 1e-5, rope_base: float = 10000.0,
+                        out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                        status: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """k3_drafter_attn_qknorm (per-head q/k RMSNorm + NeoX RoPE in the kernel)."""
+    lib = _lib.load()
+    a = _common(qkv, k_pool, v_pool, page_table, context_lens, block_lens, num_q_heads, num_kv_heads,
+                tokens_per_block, out, workspace)
+    _check(positions.dtype in POS_DTYPES and positions.dim() == 1 and positions.numel() == a["R"] * a["T"]
+           and positions.is_contiguous() and positions.device == a["dev"], "positions must be int32/int64 [R*T]")
+    for name, wt in (("q_norm_weight", q_norm_weight), ("k_norm_weight", k_norm_weight)):
+        _check(wt.dtype == torch.bfloat16 and tuple(wt.shape) == (HEAD_DIM,) and wt.is_contiguous()
+               and wt.device == a["dev"], f"{name} must be bf16 [64]")
+    scale = 1.0 / math.sqrt(HEAD_DIM) if scale is None else float(scale)
+    if status is not None:
+        _check(status.dtype == torch.int32 and status.numel() >= 1 and status.device == a["dev"],
+               "status must be an int32 GPU tensor")
+    rc = lib.drafter_attn_qknorm(
+        qkv.data_ptr(), qkv.stride(0), k_pool.data_ptr(), v_pool.data_ptr(), k_pool.stride(0), k_pool.shape[0],
+        _ptr(page_table) if a["stride"] else None, a["stride"], context_lens.data_ptr(), _ptr(block_lens),
+        a["R"], a["T"], a["Hq"], a["Hkv"], HEAD_DIM, PAGE, scale,
+        positions.data_ptr(), POS_DTYPES[positions.dtype], q_norm_weight.data_ptr(), k_norm_weight.data_ptr(),
+        float(eps), float(rope_base),
+        a["workspace"].data_ptr(), a["workspace"].numel(), a["out"].data_ptr(), a["out"].stride(0),
+        _ptr(status), _stream(a["dev"]))
+    _raise(rc)
+    return a["out"]

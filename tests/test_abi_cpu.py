@@ -1,0 +1,153 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, and its
+host-side checks reject out-of-contract calls before touching a device.
+
+No call here reaches a kernel launch: every call is either a pure host query
+(workspace size, split plan) or fails validation first.
+"""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+from speculative_decoding_drafter_amd import _lib
+from speculative_decoding_drafter_amd.build import INCLUDE
+
+HEADER = os.path.join(INCLUDE, "drafter_attn.h")
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "contract_facts.json")
+
+DA_OK, DA_EINVAL, DA_EUNSUPPORTED, DA_EWORKSPACE = 0, -1, -2, -3
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:size_t|int|const char\*)\s+(drafter_attn\w*)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_entry_points():
+    assert _declared() == sorted(["drafter_attn", "drafter_attn_qknorm", "drafter_attn_workspace_bytes",
+                                  "drafter_attn_plan", "drafter_attn_last_error"])
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+    assert set(_declared()) == set(_lib.SIGNATURES)
+
+
+def test_header_constants_match_the_pages():
+    facts = json.load(open(GOLDEN))
+    text = open(HEADER).read()
+    val = lambda n: int(re.search(rf"#define {n} (\d+)", text).group(1))
+    assert val("DA_MAX_REQUESTS") == facts["max_requests"]
+    assert val("DA_MAX_TOKENS") == facts["max_tokens_per_block"]
+    assert val("DA_HEAD_DIM") == facts["head_dim"]
+    assert val("DA_PAGE_SIZE") == facts["page_size"]
+    assert val("DA_GQA") == facts["q_heads_per_kv_head"]
+
+
+def test_workspace_bytes(lib):
+    f = lib.drafter_attn_workspace_bytes
+    for R, T, hkv, stride in [(1, 8, 1, 1), (8, 8, 1, 32), (8, 8, 4, 40), (8, 8, 4, 512), (3, 2, 4, 0)]:
+        n = f(R, T, 6 * hkv, hkv, stride)
+        s, p = ctypes.c_int32(), ctypes.c_int32()
+        assert lib.drafter_attn_plan(R, hkv, stride, ctypes.byref(s), ctypes.byref(p)) == DA_OK
+        assert n >= R * hkv * s.value * 48 * 66 * 4
+        assert n % 256 == 0
+    assert f(9, 8, 6, 1, 4) == 0          # too many requests
+    assert f(1, 9, 6, 1, 4) == 0          # too many tokens
+    assert f(1, 8, 12, 1, 4) == 0         # GQA ratio
+    assert f(1, 8, 6, 1, -1) == 0
+
+
+def test_plan_covers_the_row_and_is_data_independent(lib):
+    for R in range(1, 9):
+        for hkv in (1, 4):
+            for stride in (0, 1, 3, 32, 40, 512, 2048, 4096):
+                s, p = ctypes.c_int32(), ctypes.c_int32()
+                assert lib.drafter_attn_plan(R, hkv, stride, ctypes.byref(s), ctypes.byref(p)) == DA_OK
+                assert 1 <= s.value <= 64 and p.value >= 1
+                assert s.value * p.value >= stride
+                assert (s.value - 1) * p.value < max(stride, 1)   # no split is entirely past the row
+    assert lib.drafter_attn_plan(0, 1, 4, None, None) == DA_EINVAL
+
+
+def _call(lib, **over):
+    """A drafter_attn call with fake (never dereferenced) pointers; every case must fail validation."""
+    a = dict(qkv=0x10000, qkv_row_stride=512, k_pool=0x200000, v_pool=0x200000 + 8192, pool_page_stride=16384,
+             num_pages=4, page_table=0x900000, page_table_stride=1, context_lens=0x900100, block_lens=None,
+             R=1, T=8, Hq=6, Hkv=1, head_dim=64, page_size=64, scale=0.125, workspace=0xA00000,
+             workspace_bytes=1 << 20, out=0xB00000, out_row_stride=384, status=None, stream=None)
+    a.update(over)
+    return lib.drafter_attn(a["qkv"], a["qkv_row_stride"], a["k_pool"], a["v_pool"], a["pool_page_stride"],
+                            a["num_pages"], a["page_table"], a["page_table_stride"], a["context_lens"],
+                            a["block_lens"], a["R"], a["T"], a["Hq"], a["Hkv"], a["head_dim"], a["page_size"],
+                            a["scale"], a["workspace"], a["workspace_bytes"], a["out"], a["out_row_stride"],
+                            a["status"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(head_dim=128), DA_EUNSUPPORTED),
+    (dict(page_size=32), DA_EUNSUPPORTED),
+    (dict(Hq=12), DA_EUNSUPPORTED),
+    (dict(R=9), DA_EINVAL),
+    (dict(R=0), DA_EINVAL),
+    (dict(T=9), DA_EINVAL),
+    (dict(T=0), DA_EINVAL),
+    (dict(Hkv=0, Hq=0), DA_EINVAL),
+    (dict(Hkv=17, Hq=102), DA_EINVAL),
+    (dict(page_table_stride=-1), DA_EINVAL),
+    (dict(qkv=None), DA_EINVAL),
+    (dict(out=None), DA_EINVAL),
+    (dict(context_lens=None), DA_EINVAL),
+    (dict(page_table=None), DA_EINVAL),
+    (dict(k_pool=None), DA_EINVAL),
+    (dict(num_pages=0), DA_EINVAL),
+    (dict(pool_page_stride=4095), DA_EINVAL),
+    (dict(pool_page_stride=4100), DA_EINVAL),
+    (dict(qkv_row_stride=500), DA_EINVAL),
+    (dict(qkv_row_stride=516), DA_EINVAL),
+    (dict(out_row_stride=380), DA_EINVAL),
+    (dict(qkv=0x10008), DA_EINVAL),        # misaligned
+    (dict(out=0xB00004), DA_EINVAL),
+    (dict(scale=0.0), DA_EINVAL),
+    (dict(scale=float("inf")), DA_EINVAL),
+    (dict(scale=float("nan")), DA_EINVAL),
+    (dict(workspace=None), DA_EWORKSPACE),
+    (dict(workspace_bytes=64), DA_EWORKSPACE),
+    (dict(out=0x10000 + 256), DA_EINVAL),  # out overlaps qkv
+    (dict(out=0x200000), DA_EINVAL),       # out overlaps the pool
+    (dict(workspace=0x200000), DA_EINVAL), # workspace overlaps the pool
+    (dict(out=0xA00000 + 4096), DA_EINVAL),  # out overlaps workspace
+])
+def test_invalid_arguments_rejected_before_launch(lib, over, code):
+    assert _call(lib, **over) == code
+    assert _lib.last_error() != ""
+
+
+def test_qknorm_specific_checks(lib):
+    base = dict(qkv=0x10000, stride=512, kp=0x200000, vp=0x202000)
+
+    def q(**o):
+        a = dict(positions=0x900200, pdt=0, wq=0x900300, wk=0x900400, eps=1e-5, base=10000.0, R=1)
+        a.update(o)
+        return lib.drafter_attn_qknorm(0x10000, 512, 0x200000, 0x202000, 16384, 4, 0x900000, 1, 0x900100,
+                                       None, a["R"], 8, 6, 1, 64, 64, 0.125, a["positions"], a["pdt"],
+                                       a["wq"], a["wk"], a["eps"], a["base"], 0xA00000, 1 << 20, 0xB00000,
+                                       384, None, None)
+    assert q(positions=None) == DA_EINVAL
+    assert q(pdt=2) == DA_EINVAL
+    assert q(wq=None) == DA_EINVAL
+    assert q(wk=0x900402) == DA_EINVAL      # misaligned
+    assert q(eps=-1.0) == DA_EINVAL
+    assert q(eps=float("nan")) == DA_EINVAL
+    assert q(base=0.0) == DA_EINVAL
+    assert q(positions=0xB00000) == DA_EINVAL   # out overlaps positions
+    assert q(R=9) == DA_EINVAL

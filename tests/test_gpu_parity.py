@@ -1,0 +1,222 @@
+"""GPU parity of the HIP path against the fp64 oracle, and its bitwise invariants.
+
+Every call goes through the C ABI (ctypes binding).  Tolerance (per element):
+|gpu - oracle| <= 2e-2 + 2e-2*|oracle|, mean |err| <= 2e-3, no NaN.  The
+invariants the method fixes exactly (page placement, request isolation,
+reruns, poison, untouched inputs, the single-key case) are checked bit for bit.
+"""
+import hashlib
+
+import numpy as np
+import pytest
+import torch
+
+import drafter_synth as ds
+import oracle
+from tests.gpu_util import check, reference, run, say, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _digest(t: torch.Tensor) -> str:
+    return hashlib.sha256(t.contiguous().view(torch.uint8).cpu().numpy().tobytes()).hexdigest()
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 5])
+def test_config_parity(n):
+    case = ds.make_config(n)
+    say(f"config {n}: R={case.R} T={case.T} Hq/Hkv={case.Hq}/{case.Hkv} stride={case.stride}")
+    got = to_np(run(case))
+    torch.cuda.synchronize()
+    check(got, reference(case), f"cfg{n}")
+
+
+@pytest.mark.parametrize("n", [1, 2, 3])
+def test_config_parity_poisoned(n):
+    # NaN in every pool element / row padding the definition never reads, garbage table entries
+    case = ds.make_config(n, poison=True)
+    clean = ds.make_config(n)
+    say(f"config {n} poisoned")
+    got = run(case)
+    ref_bits = run(clean)
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref_bits), "poison changed the output bits"
+    check(to_np(got), reference(clean), f"cfg{n}-poison")
+
+
+def test_value_mean_one_diagnostic():
+    # V ~ N(1, 1): outputs are about 1, so relative errors are visible
+    case = ds.make_case(8, 8, 24, 4, [2041, 0, 1, 64, 65, 1000, 1500, 33], seed=55, qknorm=True,
+                        v_mean=1.0, pos_dtype=torch.int64, stride=40, pool_pages=300)
+    say("v-mean-1 diagnostic")
+    rel2 = check(to_np(run(case)), reference(case), "vmean1")
+    assert rel2 < 5e-3
+
+
+def test_long_context_vmean1():
+    case = ds.make_case(2, 8, 24, 4, [32768, 20000], seed=56, qknorm=True, v_mean=1.0, pool_pages=900)
+    say("long context v-mean-1")
+    rel2 = check(to_np(run(case)), reference(case), "long-vmean1")
+    assert rel2 < 5e-3
+
+
+def test_reruns_bit_identical():
+    case = ds.make_config(3)
+    g = ds.to_device(case, "cuda")
+    say("reruns")
+    first = run(case, g).clone()
+    for _ in range(20):
+        assert torch.equal(run(case, g), first)
+
+
+def test_page_permutation_bitwise():
+    # I2: the same logical context at other physical pages gives the same bits
+    case = ds.make_config(3)
+    say("page permutation")
+    base = run(case).clone()
+    P = case.num_pages
+    perm = torch.from_numpy(np.random.default_rng(3).permutation(P))
+    inv = torch.argsort(perm)
+    moved = ds.make_config(3)
+    moved.pool = case.pool[perm].contiguous()
+    moved.k_pool, moved.v_pool = moved.pool[:, 0], moved.pool[:, 1]
+    moved.page_table = inv[case.page_table.long()].to(torch.int32)
+    assert torch.equal(run(moved), base)
+
+
+def test_request_isolation_bitwise():
+    # I4: rewriting one request's rows, pages and length leaves the others' bits alone
+    case = ds.make_config(2)
+    say("request isolation")
+    base = run(case).clone()
+    k = int(np.argmax(case.context_lens.numpy()))
+    other = ds.make_config(2)
+    other.qkv[k * 8:(k + 1) * 8] = torch.randn(8, other.qkv.shape[1]).to(torch.bfloat16)
+    L = int(other.context_lens[k])
+    for pg in other.page_table[k, : -(-L // 64)].tolist():
+        other.pool[pg] = -other.pool[pg]
+    other.context_lens[k] = L // 3
+    other.positions[k * 8:(k + 1) * 8] += 1000
+    got = run(other)
+    keep = torch.ones(64, dtype=torch.bool)
+    keep[k * 8:(k + 1) * 8] = False
+    assert torch.equal(got[keep.cuda()], base[keep.cuda()])
+    assert not torch.equal(got[~keep.cuda()], base[~keep.cuda()])
+
+
+def test_inputs_untouched():
+    # I5: pool, qkv and page table are bit-identical after the call
+    case = ds.make_config(3)
+    g = ds.to_device(case, "cuda")
+    before = [_digest(g.pool), _digest(g.qkv), _digest(g.page_table), _digest(g.context_lens), _digest(g.positions)]
+    say("inputs untouched")
+    run(case, g)
+    torch.cuda.synchronize()
+    after = [_digest(g.pool), _digest(g.qkv), _digest(g.page_table), _digest(g.context_lens), _digest(g.positions)]
+    assert before == after
+
+
+@pytest.mark.parametrize("qk", [False, True])
+def test_single_key_returns_v_exactly(qk):
+    # P5: L = 0, T = 1 -> one key with weight 1 -> out == v bit for bit (v is never normalised)
+    case = ds.make_case(8, 1, 24, 4, [0] * 8, seed=19, stride=0, qknorm=qk)
+    say(f"single key qk={qk}")
+    out = run(case).cpu()
+    for h in range(24):
+        g = h // 6
+        assert torch.equal(out[:, h * 64:(h + 1) * 64], case.qkv[:, (28 + g) * 64:(29 + g) * 64])
+
+
+def test_qknorm_equals_cpu_norm_rope_then_plain():
+    # I7 on the GPU: the fused prologue vs the plain kernel on q/k normalised+rotated on the CPU
+    case = ds.make_config(3)
+    a = case.np_args()
+    qkv = a["qkv"].copy()
+    pos = a["positions"]
+    for h in range(case.Hq):
+        c = slice(h * 64, (h + 1) * 64)
+        qkv[:, c] = oracle.rope_neox(oracle.rms_norm(qkv[:, c], a["q_norm_weight"], 1e-5), pos, 1e4)
+    for g in range(case.Hkv):
+        c = slice((case.Hq + g) * 64, (case.Hq + g + 1) * 64)
+        qkv[:, c] = oracle.rope_neox(oracle.rms_norm(qkv[:, c], a["k_norm_weight"], 1e-5), pos, 1e4)
+    plain = ds.make_config(3)
+    plain.qkv = torch.from_numpy(qkv).to(torch.bfloat16)
+    plain.qknorm = False
+    say("qknorm vs cpu-prepared plain")
+    fused = to_np(run(case))
+    unfused = to_np(run(plain))
+    err = np.abs(fused - unfused)
+    assert err.max() <= 2e-2 and err.mean() <= 1e-3
+
+
+def test_block_lens_and_layout_variants():
+    # ragged blocks, separate pools, padded qkv rows (NaN padding), out with a wider row stride
+    case = ds.make_case(5, 7, 24, 4, [0, 1, 64, 1999, 130], seed=23, block_lens=[7, 1, 3, 5, 2], qknorm=True,
+                        separate_pools=True, qkv_row_pad=40, stride=37, pool_pages=64, pos_dtype=torch.int64,
+                        poison=True)
+    say("block lens / layout variants")
+    out = torch.full((35, 24 * 64 + 64), 7.0, dtype=torch.bfloat16, device="cuda")
+    run(case, out=out[:, :24 * 64 + 64])
+    got = out.float().cpu().numpy().astype(np.float64)
+    ref = reference(case)
+    check(got[:, :24 * 64], ref, "variants")
+    assert np.all(got[:, 24 * 64:] == 7.0), "wrote past the output row"
+    bl = [7, 1, 3, 5, 2]
+    for r in range(5):
+        assert np.all(got[r * 7 + bl[r]:(r + 1) * 7, :24 * 64] == 0.0)
+
+
+@pytest.mark.parametrize("R,T,hkv,lens", [
+    (1, 1, 1, [0]), (1, 8, 1, [1]), (2, 3, 4, [63, 64]), (3, 5, 1, [65, 127, 128]),
+    (8, 8, 4, [2041] * 8), (8, 2, 1, [0] * 8), (4, 8, 2, [4096, 0, 3000, 17]),
+])
+def test_edge_shapes(R, T, hkv, lens):
+    case = ds.make_case(R, T, 6 * hkv, hkv, lens, seed=sum(lens) + R * 31 + T, qknorm=True, pool_pages=None)
+    say(f"edge R={R} T={T} Hkv={hkv} L={lens}")
+    check(to_np(run(case)), reference(case), f"edge-{R}-{T}-{hkv}")
+
+
+def test_max_context_many_splits():
+    # a page-table stride long enough to hit the split cap, mixed with an empty request
+    case = ds.make_case(2, 4, 6, 1, [131072, 0], seed=77, qknorm=True, pool_pages=2100)
+    say("max context / split cap")
+    check(to_np(run(case)), reference(case), "maxctx")
+
+
+def test_status_flags_and_clamping():
+    # device-value contract breaks are clamped (no out-of-range reads) and reported
+    case = ds.make_case(2, 2, 6, 1, [100, 50], seed=5, stride=2, pool_pages=4)
+    g = ds.to_device(case, "cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    say("status flags")
+    run(case, g, status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    g.context_lens[0] = 10_000          # > stride * 64
+    g.page_table[1, 0] = 1_000_000      # page id out of range
+    run(case, g, status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) & 1 and int(status.item()) & 2
+    bl = torch.tensor([0, 9], dtype=torch.int32, device="cuda")
+    status.zero_()
+    run(case, g, status=status, block_lens=bl)
+    torch.cuda.synchronize()
+    assert int(status.item()) & 4
+
+
+def test_out_of_contract_raises():
+    from speculative_decoding_drafter_amd import DrafterAttnError
+
+    case = ds.make_config(2)
+    g = ds.to_device(case, "cuda")
+    say("out of contract")
+    with pytest.raises(DrafterAttnError):
+        run(case, g, num_q_heads=12)
+    with pytest.raises(DrafterAttnError):
+        run(case, g, scale=-1.0)
+    with pytest.raises(DrafterAttnError):
+        run(case, g, workspace=torch.zeros(16, dtype=torch.uint8, device="cuda"))
+    with pytest.raises(DrafterAttnError):   # out aliasing qkv
+        run(case, g, out=g.qkv[:, :384])
+    with pytest.raises(DrafterAttnError):
+        run(case, g, eps=float("nan"))
