@@ -1,0 +1,188 @@
+"""Benchmark of the drafter block-attention hot path on one MI355X.
+
+Default workload: 8 requests x 8 draft tokens, 24 query / 4 KV heads, head_dim 64,
+context 32768 tokens per request (512 HND pages of 64 each, 4096 pages shuffled
+across a 5000-page bf16 pool), per-head q/k RMSNorm + NeoX RoPE in the kernel.
+
+A step is one call of drafter_attn_qknorm (one kernel launch).  Inputs are
+resident in HBM before timing starts.  Before every step (warm-up and timed)
+an untimed kernel reads a 1 GiB buffer so that neither the L2 nor the 256 MB
+Infinity Cache holds the 268 MB of K/V the call reads: each timed call streams
+its pages from HBM.  (The flush only reads, so it leaves no dirty lines whose
+write-back would compete with the timed call.)  Each call is bracketed by HIP events on the
+stream it is launched on; ms_per_step is their mean.  ``--hot`` times
+back-to-back calls without the flush instead (reported, not the headline).
+
+value = algorithmic K/V bytes per call / mean call time (GB/s): every context
+K and V element is read exactly once, sum_r L_r * Hkv * 64 * 2 * 2 bytes.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=5, choices=[1, 2, 3, 5])
+    ap.add_argument("--hot", action="store_true", help="no cache flush between calls")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=10.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 512 MiB device copy (for counter calibration)")
+    return ap.parse_args()
+
+
+WORKLOADS = {
+    1: "cfg1: 1 req x 8 tok, 6/1 heads, L=64 in a 4-page pool, plain path",
+    2: "cfg2: 8 req x 8 tok, 6/1 heads, L~U[0,2041], 512-page pool, dense int32 rows, qknorm int32 pos",
+    3: "cfg3: 8 req x 8 tok, 24/4 heads, L~U[0,2041], stride-40 rows, qknorm int64 pos",
+    5: "drafter block attention qknorm, 8 req x 8 tok, 24/4 heads, L=32768/request, "
+       "4096 of 5000 pages, dense int32 rows, int32 pos",
+}
+
+
+def cpu_baseline(case, budget_s: float):
+    """Time the fp64 oracle (as it stands) on a bounded sample of the same workload."""
+    import numpy as np
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    a = case.np_args()
+    R = case.R
+    # sample: whole requests, one at a time (cycling over the batch), until the budget is used
+    done_bytes = 0
+    t0 = time.perf_counter()
+    n_req = 0
+    for it in range(1000 * R):
+        r = it % R
+        sub = dict(a)
+        sub["qkv"] = a["qkv"][r * case.T:(r + 1) * case.T]
+        sub["page_table"] = a["page_table"][r:r + 1]
+        sub["context_lens"] = a["context_lens"][r:r + 1]
+        sub["positions"] = None if a["positions"] is None else a["positions"][r * case.T:(r + 1) * case.T]
+        if case.qknorm:
+            oracle.drafter_attn_qknorm(**sub)
+        else:
+            oracle.drafter_attn(**sub)
+        n_req += 1
+        done_bytes += int(a["context_lens"][r]) * case.Hkv * 64 * 2 * 2
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n_req} request-passes over the {R} requests of the same workload "
+                      f"(fp64 numpy oracle, {n_req / R:.2f} calls' worth), {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this hot path is not sharded across GPUs "
+              "(see the design notes); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import drafter_synth as ds
+    from speculative_decoding_drafter_amd import drafter_attn, drafter_attn_qknorm, make_workspace, plan
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    case = ds.make_config(args.config)
+    g = ds.to_device(case, dev)
+    ws = make_workspace(case.R, case.T, case.Hq, case.Hkv, case.stride, dev)
+    out = torch.empty(case.R * case.T, case.Hq * 64, dtype=torch.bfloat16, device=dev)
+    kw = dict(num_q_heads=case.Hq, num_kv_heads=case.Hkv, tokens_per_block=case.T, scale=case.scale,
+              out=out, workspace=ws)
+    if case.qknorm:
+        call = lambda: drafter_attn_qknorm(g.qkv, g.k_pool, g.v_pool, g.page_table, g.context_lens, g.positions,
+                                           g.q_norm_weight, g.k_norm_weight, eps=case.eps,
+                                           rope_base=case.rope_base, **kw)
+    else:
+        call = lambda: drafter_attn(g.qkv, g.k_pool, g.v_pool, g.page_table, g.context_lens, **kw)
+
+    flush = None if args.hot else torch.ones(1 << 28, dtype=torch.int32, device=dev)
+    flush_out = torch.empty((), dtype=torch.int64, device=dev)
+
+    def one(timed_events=None):
+        if flush is not None:
+            torch.sum(flush, out=flush_out)
+        if timed_events is None:
+            call()
+        else:
+            timed_events[0].record()
+            call()
+            timed_events[1].record()
+
+    for _ in range(args.warmup):
+        one()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e in evs:
+        one(e)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    times_ms = sorted(a.elapsed_time(b) for a, b in evs)
+    mean_ms = sum(times_ms) / len(times_ms)
+    p10, p50, p90 = (times_ms[int(q * (len(times_ms) - 1))] for q in (0.1, 0.5, 0.9))
+
+    if args.calibrate_copy:
+        src = torch.empty(1 << 29, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    kv_bytes = case.kv_bytes()
+    gbs = kv_bytes / (mean_ms * 1e-3) / 1e9
+    S, Ps = plan(case.R, case.Hkv, case.stride)
+    line = {
+        "metric": "K/V-read HBM GB/s (% of MI355X peak) and us/call, 8 req x 8 tok, 24/4 heads",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(mean_ms, 6),
+        "us_per_call": round(mean_ms * 1e3, 3),
+        "us_p10_p50_p90": [round(p10 * 1e3, 3), round(p50 * 1e3, 3), round(p90 * 1e3, 3)],
+        "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "cache": "hot (no flush)" if args.hot else "cold (1 GiB read before each call)",
+        "wall_s_timed_region": round(wall, 4),
+        "config": {"workload": WORKLOADS[args.config], "requests": case.R, "tokens": case.T,
+                   "q_heads": case.Hq, "kv_heads": case.Hkv, "head_dim": 64, "page": 64,
+                   "context_lens_sum": int(case.context_lens.sum()), "pool_pages": case.num_pages,
+                   "page_table_stride": case.stride, "splits": S, "pages_per_split": Ps,
+                   "qknorm": case.qknorm, "kv_bytes_per_call": kv_bytes},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "drafter_attn_kernel<3,true,false>" if case.qknorm else "drafter_attn_kernel<3,false,false>"},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(case, args.cpu_budget_s)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -35,30 +35,33 @@ constexpr int kPage = 64;     // tokens per page
 constexpr int kG = 6;         // query heads per KV head
 constexpr int kMaxT = 8;      // tokens per block
 constexpr int kRows = 48;     // kG * kMaxT query rows per workgroup
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;                    // two per SIMD
 constexpr int kThreads = 64 * kWaves;
 constexpr int kMaxSplits = 64;
+constexpr int kMaxStride = 16384;            // pages per request row: keeps pages per wave <= 32
 constexpr int kTileBytes = kPage * kD * 2;   // one [64][64] bf16 tile, 8 KiB
+constexpr int kStageBytes = 2 * kTileBytes;  // a wave's K slot then V slot
 
 // LDS layout (bytes)
 constexpr int kOffQ = 0;                                   // [48][64] bf16 query tile
 constexpr int kOffCS = kOffQ + kRows * kD * 2;             // [8][32] (cos, sin) fp32
-constexpr int kOffMW = kOffCS + kMaxT * 32 * 8;            // [4][48] per-wave running max
-constexpr int kOffLW = kOffMW + kWaves * kRows * 4;        // [4][48] per-wave weight sum
+constexpr int kOffOwnK = kOffCS + kMaxT * 32 * 8;          // own block's K rows (8 x 128 B)
+constexpr int kOffOwnV = kOffOwnK + kMaxT * kD * 2;        // own block's V rows (8 x 128 B)
+constexpr int kOffMW = kOffOwnV + kMaxT * kD * 2;          // [8][48] per-wave running max
+constexpr int kOffLW = kOffMW + kWaves * kRows * 4;        // [8][48] per-wave weight sum
 constexpr int kOffFlag = kOffLW + kWaves * kRows * 4;      // last-workgroup flag
-constexpr int kOffU = kOffFlag + 16;                       // union region
-constexpr int kOffVT = kOffU;                              // [4 waves] V^T tiles
-constexpr int kOffKown = kOffVT + kWaves * kTileBytes;     // own-block K tile
-constexpr int kOffVown = kOffKown + kTileBytes;            // own-block V tile
+constexpr int kOffStage = 14336;                           // [8 waves][K | V] page slots
 constexpr int kObufStride = kD + 4;                        // fp32 row stride (pad: no bank conflicts)
-constexpr int kOffObuf = kOffU;                            // [4][48][68] fp32 merge buffer
-constexpr int kOffWts = kOffU;                             // [kMaxSplits][48] fp32 combine weights
-constexpr int kUnionBytes = (kWaves * kRows * kObufStride * 4 > kWaves * kTileBytes + 2 * kTileBytes)
-                                ? kWaves * kRows * kObufStride * 4
-                                : kWaves * kTileBytes + 2 * kTileBytes;
-constexpr int kSmemBytes = kOffU + kUnionBytes;
-static_assert(kMaxSplits * kRows * 4 <= kUnionBytes, "combine weights must fit the union");
-static_assert(kSmemBytes <= 64 * 1024, "LDS budget");
+constexpr int kOffObuf = kOffStage;                        // [8][48][68] fp32 merge buffer (after the loop)
+constexpr int kOffWts = kOffStage;                         // [kMaxSplits][48] fp32 combine weights
+constexpr int kSmemBytes = kOffStage + kWaves * kStageBytes;
+static_assert(kOffFlag + 16 <= kOffStage, "LDS layout");
+// the own-block tiles are read like full 64-row tiles (rows past the block are
+// masked): their 8 KiB read windows must stay inside the allocation
+static_assert(kOffOwnV + kTileBytes <= kSmemBytes, "own-block read window");
+static_assert(kWaves * kRows * kObufStride * 4 <= kWaves * kStageBytes, "merge buffer fits");
+static_assert(kMaxSplits * kRows * 4 <= kWaves * kStageBytes, "combine weights fit");
+static_assert(kSmemBytes <= 160 * 1024, "gfx950 LDS budget");
 
 typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -116,74 +119,158 @@ __device__ __forceinline__ uint16_t to_bf16(float x) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
 }
 
-// XOR swizzle of the 16-byte chunk inside a 128-byte LDS row: keeps both the
-// transposing writes (8 rows 8 apart) and the fragment reads (8 consecutive
-// rows) on distinct banks.
-__device__ __forceinline__ int swz(int row) { return ((row >> 3) ^ row) & 7; }
-
-__device__ __forceinline__ int tile_off(int row, int chunk) {
-  return row * (kD * 2) + ((chunk ^ swz(row)) << 4);
-}
-
 __device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Byte offset of LDS memory (the 32-bit address LDS instructions and M0 take).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (const __attribute__((address_space(3))) void*)(p)));
+}
+
+// A 64-bit value known to be equal in every lane, moved to SGPRs.  readfirstlane
+// works on 32-bit ints: each half is taken back as uint32_t before widening (a
+// signed widening would smear bit 31 of the low half over the high half).
+__device__ __forceinline__ uint64_t uniform_u64(uint64_t v) {
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(v))));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(v >> 32))));
+  return static_cast<uint64_t>(lo) | (static_cast<uint64_t>(hi) << 32);
+}
+
+// Four 16-byte-per-lane global -> LDS DMAs (global_load_lds_dwordx4).  The
+// instruction offset applies to both addresses: DMA j reads sbase + voff_j +
+// 1024*j and lands at lds_base + 1024*j + 16*lane.  sbase and lds_base are
+// wave-uniform (SGPRs / M0).  Issued from inline asm so that the compiler does
+// not treat every later LDS read as dependent on it (it would wait for all DMA in
+// flight); the page loop places its own vmcnt waits.
+__device__ __forceinline__ void dma16x4(uint32_t v0, uint32_t v1, uint32_t v2, uint32_t v3, const void* sbase,
+                                        uint32_t lds_base) {
+  asm volatile(
+      "s_mov_b32 m0, %5\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %4\n\t"
+      "global_load_lds_dwordx4 %1, %4 offset:1024\n\t"
+      "global_load_lds_dwordx4 %2, %4 offset:2048\n\t"
+      "global_load_lds_dwordx4 %3, %4 offset:3072"
+      :: "v"(v0), "v"(v1), "v"(v2), "v"(v3), "s"(sbase), "s"(lds_base) : "memory");
+}
+
+// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// every LDS read this wave issued has returned: its slot may be refilled by DMA
+__device__ __forceinline__ void wait_lds_reads() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// 16-byte-chunk XOR swizzles of the 128-byte rows of a staged [64 keys][64 dims]
+// tile.  K: the 8 keys a group of 8 lanes reads for one A-fragment land on 8
+// distinct chunk columns.  V: the 4 keys read together for a V^T fragment (one
+// per 16-lane group) land on 4 disjoint chunk pairs.
+__device__ __forceinline__ int swz_k(int key) { return ((key >> 3) & 3) | ((key & 1) << 2); }
+__device__ __forceinline__ int swz_v(int key) { return 2 * (key & 3); }
+// XOR swizzle of the query tile rows (fragment reads: 8 consecutive rows, one chunk)
+__device__ __forceinline__ int swz_q(int row) { return ((row >> 3) ^ row) & 7; }
+
+__device__ __forceinline__ int koff(int key, int chunk) { return key * (kD * 2) + ((chunk ^ swz_k(key)) << 4); }
+__device__ __forceinline__ int voff(int key, int chunk) { return key * (kD * 2) + ((chunk ^ swz_v(key)) << 4); }
+__device__ __forceinline__ int qoff(int row, int chunk) { return row * (kD * 2) + ((chunk ^ swz_q(row)) << 4); }
+
 // The key a lane's A-fragment row / S^T output register stands for.  The 64
-// keys of a page are permuted so that (a) the P^T registers a lane owns after
-// the score MFMA are exactly the B-fragment of the PV MFMA and (b) the V^T
-// fragment a lane needs is one contiguous 16-byte LDS chunk.  `mt` = 16-key
-// M-tile, `r16` = row inside the tile.
+// keys of a page are permuted so that the P^T registers a lane owns after the
+// score MFMA are exactly its B-fragment of the PV MFMA.  `mt` = 16-key M-tile,
+// `r16` = row inside the tile.
 __device__ __forceinline__ int key_of(int mt, int r16) {
   return 32 * (mt & 1) + 8 * (r16 & 3) + 4 * (mt >> 1) + (r16 >> 2);
 }
 
-struct KFrag { u32x4 a[4][2]; };   // [M-tile][k-step]: K rows in A-fragment layout
-struct VFrag { u32x4 v[8]; };      // [jj]: key 8*jj + lane/8, dims 8*(lane%8) .. +7
+// Stage one [64][64] bf16 tile (8 KiB contiguous in the pool) into LDS: 8 DMA
+// instructions, each reading 1 KiB (8 full rows) of global memory.  Lane l of
+// instruction jj writes row 8*jj + l/8, chunk column l%8, and reads the source
+// chunk the row's swizzle maps there.
+// Per-lane source offsets (bytes inside a tile) for stage_tile: DMA jj writes row
+// 8*jj + lane/8, chunk column lane%8; the source chunk is the one the row's swizzle
+// maps there.  Only jj % 4 matters (K) or nothing at all (V), so 4 + 1 registers
+// hold every offset.
+struct DmaOffsets {
+  uint32_t k[4];
+  uint32_t v;
+};
 
-__device__ __forceinline__ void load_k_global(KFrag& k, const uint16_t* base, int lane) {
-  const int r16 = lane & 15, lg = lane >> 4;
+__device__ __forceinline__ DmaOffsets dma_offsets(int lane) {
+  const int r0 = lane >> 3, pc = lane & 7;
+  DmaOffsets d;
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    const uint16_t* row = base + key_of(mt, r16) * kD + 8 * lg;
-    k.a[mt][0] = ld16(row);
-    k.a[mt][1] = ld16(row + 32);
+  for (int j = 0; j < 4; ++j) d.k[j] = r0 * (kD * 2) + ((pc ^ swz_k(8 * j + r0)) << 4);
+  d.v = r0 * (kD * 2) + ((pc ^ swz_v(r0)) << 4);
+  return d;
+}
+
+// Stage one [64][64] bf16 tile (8 KiB contiguous in the pool) into LDS: 8 DMA
+// instructions, each reading 1 KiB (8 full rows) of global memory.
+template <bool IS_V>
+__device__ __forceinline__ void stage_tile(const uint16_t* base, uint32_t lds, const DmaOffsets& off) {
+  const uint64_t ua = uniform_u64(reinterpret_cast<uintptr_t>(base));
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const void* sb = reinterpret_cast<const void*>(ua + 4096 * h);
+    if (IS_V)
+      dma16x4(off.v, off.v, off.v, off.v, sb, lds + 4096 * h);
+    else
+      dma16x4(off.k[0], off.k[1], off.k[2], off.k[3], sb, lds + 4096 * h);
   }
 }
 
-__device__ __forceinline__ void load_v_global(VFrag& v, const uint16_t* base, int lane) {
-  const uint16_t* p = base + (lane >> 3) * kD + 8 * (lane & 7);
-#pragma unroll
-  for (int jj = 0; jj < 8; ++jj) v.v[jj] = ld16(p + jj * 8 * kD);
-}
+struct NoHook {
+  __device__ __forceinline__ void operator()() const {}
+};
 
-__device__ __forceinline__ void load_k_lds(KFrag& k, const unsigned char* tile, int lane) {
-  const int r16 = lane & 15, lg = lane >> 4;
+// ---------------------------------------------------------------------------------
+// one page (64 keys) of online-softmax attention for one wave, 16*NT query rows,
+// from a staged K tile (kt) and V tile (vt)
+// ---------------------------------------------------------------------------------
+// Hooks let the page loop refill a slot as soon as it has been read:
+// k_read() runs once the K tile is in registers, v_wait() before the V tile is
+// read, v_read() once the V tile is in registers.
+//
+// LDS addressing: for the keys a lane reads, both swizzles reduce to a per-lane
+// term, so every read is a per-lane base plus a compile-time offset.
+//   K: key_of(mt, r16) = 32(mt&1) + 4(mt>>1) + [8(r16&3) + (r16>>2)], and
+//      swz_k(key) = (r16&3) | ((r16>>2)&1)<<2 for all mt.
+//   V: keys 8e + 4ks + lg all have key&3 = lg, so swz_v(key) = 2*lg.
+template <int NT, class KRead = NoHook, class VWait = NoHook, class VRead = NoHook>
+__device__ __forceinline__ void attend_page(const unsigned char* kt, const unsigned char* vt, int valid,
+                                            const unsigned char* qt, f32x4 (&o)[NT][4],
+                                            float (&m_run)[NT], float (&l_run)[NT], float c, int lane,
+                                            KRead k_read = {}, VWait v_wait = {}, VRead v_read = {}) {
+  const int lg = lane >> 4, r16 = lane & 15;
+  const bool tail = valid < kPage;  // wave-uniform
+  // query B-fragments (re-read from the LDS tile: fewer live registers across pages)
+  u32x4 qf[NT][2];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    const int row = key_of(mt, r16);
-    k.a[mt][0] = *reinterpret_cast<const u32x4*>(tile + tile_off(row, lg));
-    k.a[mt][1] = *reinterpret_cast<const u32x4*>(tile + tile_off(row, 4 + lg));
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+      qf[nt][ks] = *reinterpret_cast<const u32x4*>(qt + qoff(16 * nt + r16, 4 * ks + lg));
+  // ---- K A-fragments: row key_of(mt, r16), dims 32*ks + 8*lg ..
+  u32x4 ka[4][2];
+  {
+    const int sk = (r16 & 3) | (((r16 >> 2) & 1) << 2);
+    const unsigned char* kb = kt + (8 * (r16 & 3) + (r16 >> 2)) * (kD * 2);
+    const unsigned char* kb0 = kb + ((lg ^ sk) << 4);
+    const unsigned char* kb1 = kb + (((4 + lg) ^ sk) << 4);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const int row = 32 * (mt & 1) + 4 * (mt >> 1);
+      ka[mt][0] = *reinterpret_cast<const u32x4*>(kb0 + row * (kD * 2));
+      ka[mt][1] = *reinterpret_cast<const u32x4*>(kb1 + row * (kD * 2));
+    }
   }
-}
-
-__device__ __forceinline__ void load_v_lds(VFrag& v, const unsigned char* tile, int lane) {
-#pragma unroll
-  for (int jj = 0; jj < 8; ++jj)
-    v.v[jj] = *reinterpret_cast<const u32x4*>(tile + tile_off(8 * jj + (lane >> 3), lane & 7));
-}
-
-// ---------------------------------------------------------------------------------
-// one page (64 keys) of online-softmax attention for one wave, 16*NT query rows
-// ---------------------------------------------------------------------------------
-template <int NT, bool TAIL>
-__device__ __forceinline__ void attend_page(const KFrag& k, VFrag& v, int valid,
-                                            const u32x4 (&qf)[NT][2], f32x4 (&o)[NT][4],
-                                            float (&m_run)[NT], float (&l_run)[NT], float c,
-                                            unsigned char* vt, int lane) {
-  const int lg = lane >> 4;
   // ---- S^T = K . Q^T  (rows: keys, cols: query rows)
   f32x4 s[NT][4];
 #pragma unroll
@@ -191,11 +278,12 @@ __device__ __forceinline__ void attend_page(const KFrag& k, VFrag& v, int valid,
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      acc = mfma(k.a[mt][0], qf[nt][0], acc);
-      acc = mfma(k.a[mt][1], qf[nt][1], acc);
+      acc = mfma(ka[mt][0], qf[nt][0], acc);
+      acc = mfma(ka[mt][1], qf[nt][1], acc);
       s[nt][mt] = acc;
     }
-  if (TAIL) {
+  k_read();
+  if (tail) {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -207,8 +295,40 @@ __device__ __forceinline__ void attend_page(const KFrag& k, VFrag& v, int valid,
         }
       }
   }
-  // ---- online softmax per query column (lane & 15), exp2 domain
-  u32x4 pf[NT][2];
+  // ---- V^T A-fragments: row d = 16*md + r16; keys 8e + 4ks + lg, e = 0..7 (16-bit reads)
+  v_wait();
+  u32x4 va[4][2];
+  {
+    const unsigned char* vb = vt + lg * (kD * 2) + (r16 & 7) * 2;
+#pragma unroll
+    for (int md = 0; md < 4; ++md) {
+      const unsigned short* vm =
+          reinterpret_cast<const unsigned short*>(vb + (((2 * md + (r16 >> 3)) ^ (2 * lg)) << 4));
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int k0 = 16 * q + 4 * ks;  // + lg, folded into the base
+          const uint32_t lo = vm[k0 * kD];
+          const uint32_t hi = vm[(k0 + 8) * kD];
+          va[md][ks][q] = lo | (hi << 16);
+        }
+    }
+  }
+  v_read();
+  if (tail) {
+    // slots past the length may hold anything (NaN): zero their values
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int k0 = 16 * q + 4 * ks + lg;
+        const uint32_t m = (k0 < valid ? 0x0000ffffu : 0u) | (k0 + 8 < valid ? 0xffff0000u : 0u);
+#pragma unroll
+        for (int md = 0; md < 4; ++md) va[md][ks][q] &= m;
+      }
+  }
+  // ---- per query N-tile: online softmax (exp2 domain), then O^T += V^T . P^T
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     float mx = s[nt][0][0];
@@ -222,70 +342,31 @@ __device__ __forceinline__ void attend_page(const KFrag& k, VFrag& v, int valid,
     const float alpha = fast_exp2((m_run[nt] - m_new) * c);
     m_run[nt] = m_new;
     const float nmc = -m_new * c;
-    float p[4][4];
+    float pr[4][4];
     float lsum = 0.f;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        p[mt][i] = fast_exp2(fmaf(s[nt][mt][i], c, nmc));
-        lsum += p[mt][i];
+        pr[mt][i] = fast_exp2(fmaf(s[nt][mt][i], c, nmc));
+        lsum += pr[mt][i];
       }
     l_run[nt] = fmaf(l_run[nt], alpha, lsum);
-#pragma unroll
-    for (int md = 0; md < 4; ++md) o[nt][md] *= alpha;
+    u32x4 pf[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      pf[nt][ks][0] = pack_bf16x2(p[2 * ks][0], p[2 * ks][1]);
-      pf[nt][ks][1] = pack_bf16x2(p[2 * ks][2], p[2 * ks][3]);
-      pf[nt][ks][2] = pack_bf16x2(p[2 * ks + 1][0], p[2 * ks + 1][1]);
-      pf[nt][ks][3] = pack_bf16x2(p[2 * ks + 1][2], p[2 * ks + 1][3]);
+      pf[ks][0] = pack_bf16x2(pr[2 * ks][0], pr[2 * ks][1]);
+      pf[ks][1] = pack_bf16x2(pr[2 * ks][2], pr[2 * ks][3]);
+      pf[ks][2] = pack_bf16x2(pr[2 * ks + 1][0], pr[2 * ks + 1][1]);
+      pf[ks][3] = pack_bf16x2(pr[2 * ks + 1][2], pr[2 * ks + 1][3]);
+    }
+#pragma unroll
+    for (int md = 0; md < 4; ++md) {
+      o[nt][md] *= alpha;
+      o[nt][md] = mfma(va[md][0], pf[0], o[nt][md]);
+      o[nt][md] = mfma(va[md][1], pf[1], o[nt][md]);
     }
   }
-  // ---- V^T through this wave's LDS tile
-  const int cgrp = lane >> 3, u = lane & 7;
-  if (TAIL) {
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj)
-      if (8 * jj + cgrp >= valid) v.v[jj] = u32x4{0u, 0u, 0u, 0u};
-  }
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-    u32x4 w;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      w[q] = __builtin_amdgcn_perm(v.v[2 * q + 1][e >> 1], v.v[2 * q][e >> 1], sel);
-    *reinterpret_cast<u32x4*>(vt + tile_off(8 * u + e, cgrp)) = w;
-  }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-  for (int md = 0; md < 4; ++md) {
-    const int d = 16 * md + (lane & 15);
-    const u32x4 a0 = *reinterpret_cast<const u32x4*>(vt + tile_off(d, lg));
-    const u32x4 a1 = *reinterpret_cast<const u32x4*>(vt + tile_off(d, 4 + lg));
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      o[nt][md] = mfma(a0, pf[nt][0], o[nt][md]);
-      o[nt][md] = mfma(a1, pf[nt][1], o[nt][md]);
-    }
-  }
-  // the next page's transposing writes must not pass these reads
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-template <int NT>
-__device__ __forceinline__ void attend(const KFrag& k, VFrag& v, int valid, const u32x4 (&qf)[NT][2],
-                                       f32x4 (&o)[NT][4], float (&m_run)[NT], float (&l_run)[NT],
-                                       float c, unsigned char* vt, int lane) {
-  if (valid >= kPage)
-    attend_page<NT, false>(k, v, valid, qf, o, m_run, l_run, c, vt, lane);
-  else
-    attend_page<NT, true>(k, v, valid, qf, o, m_run, l_run, c, vt, lane);
 }
 
 __device__ __forceinline__ void flag(int32_t* status, int bit) {
@@ -340,7 +421,7 @@ __device__ __forceinline__ u32x4 pack8(const float (&x)[8]) {
 // ---------------------------------------------------------------------------------
 template <int NT, bool QKNORM, bool POS64>
 __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[kSmemBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kSmemBytes];
   const int s = blockIdx.x, g = blockIdx.y, r = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -367,6 +448,31 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
   const int pbeg = s * p.Ps;
   const int pend = min(npg, pbeg + p.Ps);
   const bool own = (s == p.S - 1);
+  // the block's own keys go to a wave with the fewest pages of this split
+  const int own_wave = max(0, pend - pbeg) & (kWaves - 1);
+
+  // This wave's pages are pbeg+w, pbeg+w+8, ... (< pend): at most 32 of them (the
+  // plan keeps pages_per_split <= 256), so one VGPR holds every page id and the
+  // page loop reads them with readlane, with no memory access of its own.
+  const int first = pbeg + w;
+  const int cnt = first < pend ? (pend - first + kWaves - 1) / kWaves : 0;
+  int id = 0;
+  if (lane < cnt) {
+    id = p.page_table[static_cast<int64_t>(r) * p.pt_stride + first + kWaves * lane];
+    if (id < 0 || id >= p.num_pages) {
+      flag(p.status, DA_FLAG_PAGE_ID);
+      id = id < 0 ? 0 : p.num_pages - 1;
+    }
+  }
+  const int64_t head_off = static_cast<int64_t>(g) * kPage * kD;
+  unsigned char* kslot = smem + kOffStage + w * kStageBytes;
+  unsigned char* vslot = kslot + kTileBytes;
+  const uint32_t lds_k = __builtin_amdgcn_readfirstlane(lds_addr(kslot));
+  const uint32_t lds_v = lds_k + kTileBytes;
+  auto page_off = [&](int i) {
+    return static_cast<int64_t>(__builtin_amdgcn_readlane(id, i)) * p.page_stride + head_off;
+  };
+  const DmaOffsets doff = dma_offsets(lane);
 
   float2* cs = reinterpret_cast<float2*>(smem + kOffCS);
   // ---- a2/a3 (qknorm): rotation table, one (token, frequency) per thread
@@ -386,7 +492,7 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
     __syncthreads();
   }
 
-  // ---- a4: query tile (and own-block K/V tiles) into LDS
+  // ---- a4: query tile (and the own block's K/V rows) into LDS; 8 lanes per row
   {
     const int sub = tid >> 3, u = tid & 7;
     unsigned char* qt = smem + kOffQ;
@@ -398,34 +504,30 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
         unpack8(ld16(p.qkv + static_cast<int64_t>(r * T + t) * p.qkv_stride + h * kD + 8 * u), x);
         if (QKNORM) norm_rope_row(x, p.wq, p.eps, cs + t * 32, u);
       }
-      *reinterpret_cast<u32x4*>(qt + tile_off(n, u)) = pack8(x);
+      *reinterpret_cast<u32x4*>(qt + qoff(n, u)) = pack8(x);
     }
-    if (own) {
-      unsigned char* kt = smem + kOffKown;
-      unsigned char* vtile = smem + kOffVown;
-      for (int item = sub; item < 2 * kPage; item += kThreads / 8) {
-        const int j = item & (kPage - 1);
-        const bool is_v = item >= kPage;
-        float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        if (j < b) {
-          const int col = (is_v ? (p.Hq + p.Hkv + g) : (p.Hq + g)) * kD + 8 * u;
-          unpack8(ld16(p.qkv + static_cast<int64_t>(r * T + j) * p.qkv_stride + col), x);
-          if (QKNORM && !is_v) norm_rope_row(x, p.wk, p.eps, cs + j * 32, u);
-        }
-        *reinterpret_cast<u32x4*>((is_v ? vtile : kt) + tile_off(j, u)) = pack8(x);
+    if (own && sub >= 48 && sub < 48 + 2 * kMaxT) {
+      // rows j < 8 of the own block's K (RMSNorm + RoPE in the qknorm variant) and V,
+      // laid out like staged tiles; rows past b are zero, rows past 8 are never valid
+      const int j = (sub - 48) & (kMaxT - 1);
+      const bool is_v = sub >= 48 + kMaxT;
+      float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      if (j < b) {
+        const int col = (is_v ? (p.Hq + p.Hkv + g) : (p.Hq + g)) * kD + 8 * u;
+        unpack8(ld16(p.qkv + static_cast<int64_t>(r * T + j) * p.qkv_stride + col), x);
+        if (QKNORM && !is_v) norm_rope_row(x, p.wk, p.eps, cs + j * 32, u);
       }
+      *reinterpret_cast<u32x4*>(is_v ? smem + kOffOwnV + voff(j, u) : smem + kOffOwnK + koff(j, u)) = pack8(x);
     }
+  }
+  // each wave's first page in flight while the workgroup synchronises
+  if (cnt > 0) {
+    stage_tile<false>(p.kpool + page_off(0), lds_k, doff);
+    stage_tile<true>(p.vpool + page_off(0), lds_v, doff);
   }
   __syncthreads();
 
-  // query B-fragments: column (lane & 15) of N-tile nt, dims 32*ks + 8*(lane>>4) ..
-  u32x4 qf[NT][2];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-      qf[nt][ks] = *reinterpret_cast<const u32x4*>(smem + kOffQ + tile_off(16 * nt + (lane & 15), 4 * ks + (lane >> 4)));
-
+  const unsigned char* qt = smem + kOffQ;
   f32x4 o[NT][4];
   float m_run[NT], l_run[NT];
 #pragma unroll
@@ -435,57 +537,41 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
 #pragma unroll
     for (int md = 0; md < 4; ++md) o[nt][md] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  unsigned char* vt = smem + kOffVT + w * kTileBytes;
 
-  // ---- a10: the block's own keys (one 64-slot pseudo-page, b valid), on the least loaded wave
-  const int npages_split = max(0, pend - pbeg);
-  if (own && w == (npages_split & (kWaves - 1))) {
-    KFrag k;
-    VFrag v;
-    load_k_lds(k, smem + kOffKown, lane);
-    load_v_lds(v, smem + kOffVown, lane);
-    attend<NT>(k, v, b, qf, o, m_run, l_run, p.c, vt, lane);
-  }
+  // ---- a10: the block's own keys (a 64-slot pseudo-page with b valid keys)
+  if (own && w == own_wave)
+    attend_page<NT>(smem + kOffOwnK, smem + kOffOwnV, b, qt, o, m_run, l_run, p.c, lane);
 
-  // ---- a5..a9: context pages, next page's loads in flight during the current one
+  // ---- a5..a9: context pages.  One K slot and one V slot per wave, each refilled
+  // with the next page as soon as it has been read, so the next page's DMA runs
+  // under the rest of this page's work (and the other wave on the SIMD).  Only the
+  // request's last page can be partial; if this wave owns it, it is its last one.
   {
-    const int32_t* prow = p.page_table + static_cast<int64_t>(r) * p.pt_stride;
-    const int64_t head_off = static_cast<int64_t>(g) * kPage * kD;
-    auto page_base = [&](int j, const uint16_t* pool) -> const uint16_t* {
-      int phys = prow[j];
-      if (phys < 0 || phys >= p.num_pages) {
-        flag(p.status, DA_FLAG_PAGE_ID);
-        phys = phys < 0 ? 0 : p.num_pages - 1;
-      }
-      return pool + static_cast<int64_t>(phys) * p.page_stride + head_off;
-    };
-    int j = pbeg + w;
-    KFrag kA, kB;
-    VFrag vA, vB;
-    if (j < pend) {
-      load_k_global(kA, page_base(j, p.kpool), lane);
-      load_v_global(vA, page_base(j, p.vpool), lane);
-    }
-    while (j < pend) {
-      int jn = j + kWaves;
-      if (jn < pend) {
-        load_k_global(kB, page_base(jn, p.kpool), lane);
-        load_v_global(vB, page_base(jn, p.vpool), lane);
-      }
-      attend<NT>(kA, vA, L - j * kPage, qf, o, m_run, l_run, p.c, vt, lane);
-      j = jn;
-      if (j >= pend) break;
-      jn = j + kWaves;
-      if (jn < pend) {
-        load_k_global(kA, page_base(jn, p.kpool), lane);
-        load_v_global(vA, page_base(jn, p.vpool), lane);
-      }
-      attend<NT>(kB, vB, L - j * kPage, qf, o, m_run, l_run, p.c, vt, lane);
-      j = jn;
+    const bool tail = cnt > 0 && first + kWaves * (cnt - 1) == npg - 1 && (L & (kPage - 1)) != 0;
+    for (int i = 0; i < cnt; ++i) {
+      const bool more = i + 1 < cnt;
+      wait_vmcnt<8>();  // this page's K landed (its V may still be in flight)
+      auto k_read = [&]() {
+        if (more) {
+          wait_lds_reads();
+          stage_tile<false>(p.kpool + page_off(i + 1), lds_k, doff);
+        }
+      };
+      auto v_wait = [&]() {
+        if (more) wait_vmcnt<8>(); else wait_vmcnt<0>();
+      };
+      auto v_read = [&]() {
+        if (more) {
+          wait_lds_reads();
+          stage_tile<true>(p.vpool + page_off(i + 1), lds_v, doff);
+        }
+      };
+      const int valid = (tail && i == cnt - 1) ? L - (npg - 1) * kPage : kPage;
+      attend_page<NT>(kslot, vslot, valid, qt, o, m_run, l_run, p.c, lane, k_read, v_wait, v_read);
     }
   }
 
-  // ---- merge the 4 waves (fixed order) into this workgroup's partial
+  // ---- merge the waves (fixed order) into this workgroup's partial
   float* mW = reinterpret_cast<float*>(smem + kOffMW);
   float* lW = reinterpret_cast<float*>(smem + kOffLW);
 #pragma unroll
@@ -500,12 +586,14 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
       lW[w * kRows + 16 * nt + lane] = l_run[nt];
     }
   }
-  __syncthreads();  // also: every wave is done with its V^T tile and the own-block tiles
+  __syncthreads();  // also: every wave is done with its page slots
   float* obuf = reinterpret_cast<float*>(smem + kOffObuf);
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int col = 16 * nt + (lane & 15);
-    const float M = fmaxf(fmaxf(mW[col], mW[kRows + col]), fmaxf(mW[2 * kRows + col], mW[3 * kRows + col]));
+    float M = mW[col];
+#pragma unroll
+    for (int ww = 1; ww < kWaves; ++ww) M = fmaxf(M, mW[ww * kRows + col]);
     const float f = (m_run[nt] == -INFINITY) ? 0.f : fast_exp2((m_run[nt] - M) * p.c);
 #pragma unroll
     for (int md = 0; md < 4; ++md) {
@@ -514,16 +602,18 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
     }
   }
   __syncthreads();
+  // The partial is published with agent-scope stores (coherent across the XCDs'
+  // L2s without a cache write-back), completed before the counter increment; the
+  // last workgroup reads it back with agent-scope loads.
   const int rgs = rg * p.S + s;
   {
     float* po = p.part_o + static_cast<int64_t>(rgs) * kRows * kD;
-    for (int idx = tid; idx < 16 * NT * (kD / 4); idx += kThreads) {
-      const int col = idx >> 4, d4 = (idx & 15) * 4;
-      f32x4 acc = *reinterpret_cast<const f32x4*>(obuf + col * kObufStride + d4);
+    for (int idx = tid; idx < 16 * NT * kD; idx += kThreads) {
+      const int col = idx >> 6, d = idx & (kD - 1);
+      float acc = obuf[col * kObufStride + d];
 #pragma unroll
-      for (int ww = 1; ww < kWaves; ++ww)
-        acc += *reinterpret_cast<const f32x4*>(obuf + (ww * kRows + col) * kObufStride + d4);
-      *reinterpret_cast<f32x4*>(po + col * kD + d4) = acc;
+      for (int ww = 1; ww < kWaves; ++ww) acc += obuf[(ww * kRows + col) * kObufStride + d];
+      __hip_atomic_store(po + idx, acc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     if (tid < 16 * NT) {
       const int col = tid;
@@ -537,24 +627,23 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
         Ls += (mw == -INFINITY) ? 0.f : lW[ww * kRows + col] * fast_exp2((mw - M) * p.c);
       }
       float* pm = p.part_ml + (static_cast<int64_t>(rgs) * kRows + col) * 2;
-      pm[0] = M;
-      pm[1] = Ls;
+      __hip_atomic_store(pm, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(pm + 1, Ls, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 
   // ---- a11/a12: the last workgroup of (r, g) merges the splits
-  __threadfence();
+  wait_vmcnt<0>();  // this thread's partial stores are complete (visible at agent scope)
   __syncthreads();
   int* last = reinterpret_cast<int*>(smem + kOffFlag);
   if (tid == 0) {
-    const uint32_t prev = atomicAdd(p.counters + rg, 1u);
+    const uint32_t prev = __hip_atomic_fetch_add(p.counters + rg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const int is_last = (prev == static_cast<uint32_t>(p.S - 1));
-    if (is_last) atomicExch(p.counters + rg, 0u);
+    if (is_last) __hip_atomic_store(p.counters + rg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     *last = is_last;
   }
   __syncthreads();
   if (!*last) return;
-  __threadfence();
 
   float* wts = reinterpret_cast<float*>(smem + kOffWts);
   const int S = p.S;
@@ -562,13 +651,15 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
     const int col = tid;
     const float* ml = p.part_ml + (static_cast<int64_t>(rg) * S * kRows + col) * 2;
     float M = -INFINITY;
-    for (int ss = 0; ss < S; ++ss) M = fmaxf(M, ml[ss * kRows * 2]);
+    for (int ss = 0; ss < S; ++ss)
+      M = fmaxf(M, __hip_atomic_load(ml + ss * kRows * 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
     float den = 0.f;
     for (int ss = 0; ss < S; ++ss) {
-      const float m = ml[ss * kRows * 2];
+      const float m = __hip_atomic_load(ml + ss * kRows * 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const float l = __hip_atomic_load(ml + ss * kRows * 2 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       const float e = (m == -INFINITY) ? 0.f : fast_exp2((m - M) * p.c);
       wts[ss * kRows + col] = e;
-      den = fmaf(ml[ss * kRows * 2 + 1], e, den);
+      den = fmaf(l, e, den);
     }
     const float inv = 1.0f / den;
     for (int ss = 0; ss < S; ++ss) wts[ss * kRows + col] *= inv;
@@ -580,8 +671,22 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
     const int t = col / kG, hh = col - kG * t;
     float acc = 0.f;
     if (t < b) {
-      for (int ss = 0; ss < S; ++ss)
-        acc = fmaf(wts[ss * kRows + col], po[(static_cast<int64_t>(ss) * kRows + col) * kD + d], acc);
+      const float* src = po + col * kD + d;
+      int ss = 0;
+      for (; ss + 8 <= S; ss += 8) {
+        float v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          v[k] = __hip_atomic_load(src + static_cast<int64_t>(ss + k) * kRows * kD, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc = fmaf(wts[(ss + k) * kRows + col], v[k], acc);
+      }
+      for (; ss < S; ++ss)
+        acc = fmaf(wts[ss * kRows + col],
+                   __hip_atomic_load(src + static_cast<int64_t>(ss) * kRows * kD, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT),
+                   acc);
     }
     p.out[static_cast<int64_t>(r * T + t) * p.out_stride + (kG * g + hh) * kD + d] = to_bf16(acc);
   }
@@ -674,6 +779,7 @@ int check_sizes(int R, int T, int Hq, int Hkv, int head_dim, int page_size, int 
   if (Hkv < 1 || Hkv > DA_MAX_KV_HEADS) return fail(DA_EINVAL, "num_kv_heads must be in [1, 16]");
   if (Hq != kG * Hkv) return fail(DA_EUNSUPPORTED, "num_q_heads must be 6 * num_kv_heads");
   if (stride < 0) return fail(DA_EINVAL, "page_table_stride must be >= 0");
+  if (stride > kMaxStride) return fail(DA_EINVAL, "page_table_stride above 16384 pages (1M tokens) is not supported");
   return DA_OK;
 }
 
@@ -785,7 +891,7 @@ size_t drafter_attn_workspace_bytes(int32_t num_requests, int32_t tokens_per_blo
 int drafter_attn_plan(int32_t num_requests, int32_t num_kv_heads, int32_t page_table_stride,
                       int32_t* num_splits, int32_t* pages_per_split) {
   if (num_requests < 1 || num_requests > DA_MAX_REQUESTS || num_kv_heads < 1 ||
-      num_kv_heads > DA_MAX_KV_HEADS || page_table_stride < 0)
+      num_kv_heads > DA_MAX_KV_HEADS || page_table_stride < 0 || page_table_stride > kMaxStride)
     return fail(DA_EINVAL, "plan: sizes outside the contract");
   const Plan plan = make_plan(num_requests, num_kv_heads, page_table_stride);
   if (num_splits) *num_splits = plan.S;

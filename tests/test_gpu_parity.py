@@ -220,3 +220,26 @@ def test_out_of_contract_raises():
         run(case, g, out=g.qkv[:, :384])
     with pytest.raises(DrafterAttnError):
         run(case, g, eps=float("nan"))
+
+
+@pytest.mark.parametrize("low_word", [0x80000000, 0xFFFF0000])
+def test_pool_at_high_addresses(low_word):
+    # Regression: page base addresses are moved to SGPRs 32 bits at a time; a signed
+    # widening of the low half once smeared bit 31 into the high half.  Place the
+    # pool where the low word has bit 31 set (and where pages straddle a 4 GiB line).
+    case = ds.make_config(2)
+    pool = case.pool
+    nbytes = pool.numel() * pool.element_size()
+    buf = torch.empty(nbytes + (1 << 33), dtype=torch.uint8, device="cuda")
+    base = buf.data_ptr()
+    off = (low_word - (base & 0xFFFFFFFF)) % (1 << 32)
+    off -= off % 4096
+    assert off + nbytes <= buf.numel()
+    view = buf[off:off + nbytes].view(torch.bfloat16).view(pool.shape)
+    view.copy_(pool.to("cuda"))
+    say(f"pool at 0x{view.data_ptr():x}")
+    assert (view.data_ptr() & 0x80000000) != 0
+    g = ds.to_device(case, "cuda")
+    g.pool = view
+    g.k_pool, g.v_pool = view[:, 0], view[:, 1]
+    check(to_np(run(case, g)), reference(case), f"highaddr-{low_word:x}")
