@@ -114,12 +114,12 @@ def main():
     else:
         call = lambda: drafter_attn(g.qkv, g.k_pool, g.v_pool, g.page_table, g.context_lens, **kw)
 
-    flush = None if args.hot else torch.ones(1 << 28, dtype=torch.int32, device=dev)
-    flush_out = torch.empty((), dtype=torch.int64, device=dev)
+    flush = None if args.hot else torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    flush_out = torch.empty((), dtype=torch.float32, device=dev)
 
     def one(timed_events=None):
         if flush is not None:
-            torch.sum(flush, out=flush_out)
+            torch.sum(flush, dim=0, out=flush_out)
         if timed_events is None:
             call()
         else:

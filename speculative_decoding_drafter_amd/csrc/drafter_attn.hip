@@ -41,6 +41,7 @@ constexpr int kMaxSplits = 64;
 constexpr int kMaxStride = 16384;            // pages per request row: keeps pages per wave <= 32
 constexpr int kTileBytes = kPage * kD * 2;   // one [64][64] bf16 tile, 8 KiB
 constexpr int kStageBytes = 2 * kTileBytes;  // a wave's K slot then V slot
+constexpr float kRescaleLog2 = 8.0f;         // lazy-rescale headroom (exp2 units)
 
 // LDS layout (bytes)
 constexpr int kOffQ = 0;                                   // [48][64] bf16 query tile
@@ -50,12 +51,13 @@ constexpr int kOffOwnV = kOffOwnK + kMaxT * kD * 2;        // own block's V rows
 constexpr int kOffMW = kOffOwnV + kMaxT * kD * 2;          // [8][48] per-wave running max
 constexpr int kOffLW = kOffMW + kWaves * kRows * 4;        // [8][48] per-wave weight sum
 constexpr int kOffFlag = kOffLW + kWaves * kRows * 4;      // last-workgroup flag
+constexpr int kOffProg = kOffFlag + 16;                    // [8] pages done per wave
 constexpr int kOffStage = 14336;                           // [8 waves][K | V] page slots
 constexpr int kObufStride = kD + 4;                        // fp32 row stride (pad: no bank conflicts)
 constexpr int kOffObuf = kOffStage;                        // [8][48][68] fp32 merge buffer (after the loop)
 constexpr int kOffWts = kOffStage;                         // [kMaxSplits][48] fp32 combine weights
 constexpr int kSmemBytes = kOffStage + kWaves * kStageBytes;
-static_assert(kOffFlag + 16 <= kOffStage, "LDS layout");
+static_assert(kOffProg + 4 * kWaves <= kOffStage, "LDS layout");
 // the own-block tiles are read like full 64-row tiles (rows past the block are
 // masked): their 8 KiB read windows must stay inside the allocation
 static_assert(kOffOwnV + kTileBytes <= kSmemBytes, "own-block read window");
@@ -66,6 +68,9 @@ static_assert(kSmemBytes <= 160 * 1024, "gfx950 LDS budget");
 typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 struct Params {
   const uint16_t* qkv;
@@ -107,12 +112,9 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// fp32 -> bf16 bits, round to nearest even (gfx950 converts in hardware)
+// two fp32 -> packed bf16 bits, round to nearest even (one v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  __bf16 a = static_cast<__bf16>(lo);
-  __bf16 b = static_cast<__bf16>(hi);
-  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, a)) |
-         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b)) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
 }
 
 __device__ __forceinline__ uint16_t to_bf16(float x) {
@@ -170,10 +172,10 @@ __device__ __forceinline__ void wait_lds_reads() { asm volatile("s_waitcnt lgkmc
 
 // 16-byte-chunk XOR swizzles of the 128-byte rows of a staged [64 keys][64 dims]
 // tile.  K: the 8 keys a group of 8 lanes reads for one A-fragment land on 8
-// distinct chunk columns.  V: the 4 keys read together for a V^T fragment (one
-// per 16-lane group) land on 4 disjoint chunk pairs.
+// distinct chunk columns.  V: the 4 keys one 16-lane group reads together in a
+// transposing read (keys 8j + const, j = 0..3) land on 4 disjoint chunk pairs.
 __device__ __forceinline__ int swz_k(int key) { return ((key >> 3) & 3) | ((key & 1) << 2); }
-__device__ __forceinline__ int swz_v(int key) { return 2 * (key & 3); }
+__device__ __forceinline__ int swz_v(int key) { return 2 * (((key >> 3) ^ key) & 3); }
 // XOR swizzle of the query tile rows (fragment reads: 8 consecutive rows, one chunk)
 __device__ __forceinline__ int swz_q(int row) { return ((row >> 3) ^ row) & 7; }
 
@@ -195,19 +197,20 @@ __device__ __forceinline__ int key_of(int mt, int r16) {
 // chunk the row's swizzle maps there.
 // Per-lane source offsets (bytes inside a tile) for stage_tile: DMA jj writes row
 // 8*jj + lane/8, chunk column lane%8; the source chunk is the one the row's swizzle
-// maps there.  Only jj % 4 matters (K) or nothing at all (V), so 4 + 1 registers
-// hold every offset.
+// maps there.  Only jj % 4 matters, so 4 + 4 registers hold every offset.
 struct DmaOffsets {
   uint32_t k[4];
-  uint32_t v;
+  uint32_t v[4];
 };
 
 __device__ __forceinline__ DmaOffsets dma_offsets(int lane) {
   const int r0 = lane >> 3, pc = lane & 7;
   DmaOffsets d;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) d.k[j] = r0 * (kD * 2) + ((pc ^ swz_k(8 * j + r0)) << 4);
-  d.v = r0 * (kD * 2) + ((pc ^ swz_v(r0)) << 4);
+  for (int j = 0; j < 4; ++j) {
+    d.k[j] = r0 * (kD * 2) + ((pc ^ swz_k(8 * j + r0)) << 4);
+    d.v[j] = r0 * (kD * 2) + ((pc ^ swz_v(8 * j + r0)) << 4);
+  }
   return d;
 }
 
@@ -220,7 +223,7 @@ __device__ __forceinline__ void stage_tile(const uint16_t* base, uint32_t lds, c
   for (int h = 0; h < 2; ++h) {
     const void* sb = reinterpret_cast<const void*>(ua + 4096 * h);
     if (IS_V)
-      dma16x4(off.v, off.v, off.v, off.v, sb, lds + 4096 * h);
+      dma16x4(off.v[0], off.v[1], off.v[2], off.v[3], sb, lds + 4096 * h);
     else
       dma16x4(off.k[0], off.k[1], off.k[2], off.k[3], sb, lds + 4096 * h);
   }
@@ -295,23 +298,29 @@ __device__ __forceinline__ void attend_page(const unsigned char* kt, const unsig
         }
       }
   }
-  // ---- V^T A-fragments: row d = 16*md + r16; keys 8e + 4ks + lg, e = 0..7 (16-bit reads)
+  // ---- V^T A-fragments: row d = 16*md + r16; keys 8e + 4ks + lg, e = 0..7.
+  // ds_read_b64_tr_b16 transposes inside each 16-lane group: destination lane
+  // 4a + c gets element c of the 8 bytes addressed by lanes 4j + a (j = 0..3).  So
+  // lane 4j + a points at V[key_j][16 md + 4a .. +3] with key_j = 8(j + 4h) + 4ks
+  // + lg, and every lane receives the 4 keys of its own dimension d.
   v_wait();
   u32x4 va[4][2];
   {
-    const unsigned char* vb = vt + lg * (kD * 2) + (r16 & 7) * 2;
+    const int j = r16 >> 2, a = r16 & 3;
+    const int t = j ^ lg;  // swz_v(key_j) / 2 for every key this lane addresses
+    const unsigned char* vrow = vt + (8 * j + lg) * (kD * 2) + 8 * (a & 1);
 #pragma unroll
     for (int md = 0; md < 4; ++md) {
-      const unsigned short* vm =
-          reinterpret_cast<const unsigned short*>(vb + (((2 * md + (r16 >> 3)) ^ (2 * lg)) << 4));
+      const unsigned char* vm = vrow + (((2 * md + (a >> 1)) ^ (2 * t)) << 4);
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int k0 = 16 * q + 4 * ks;  // + lg, folded into the base
-          const uint32_t lo = vm[k0 * kD];
-          const uint32_t hi = vm[(k0 + 8) * kD];
-          va[md][ks][q] = lo | (hi << 16);
+        for (int h = 0; h < 2; ++h) {
+          const i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4*)(vm + (32 * h + 4 * ks) * (kD * 2)));
+          const uint64_t bits = __builtin_bit_cast(uint64_t, x);
+          va[md][ks][2 * h] = static_cast<uint32_t>(bits);
+          va[md][ks][2 * h + 1] = static_cast<uint32_t>(bits >> 32);
         }
     }
   }
@@ -322,13 +331,17 @@ __device__ __forceinline__ void attend_page(const unsigned char* kt, const unsig
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int k0 = 16 * q + 4 * ks + lg;
+        const int k0 = 16 * q + 4 * ks + lg;  // element e = 2q (low half); e = 2q + 1 is k0 + 8
         const uint32_t m = (k0 < valid ? 0x0000ffffu : 0u) | (k0 + 8 < valid ? 0xffff0000u : 0u);
 #pragma unroll
         for (int md = 0; md < 4; ++md) va[md][ks][q] &= m;
       }
   }
-  // ---- per query N-tile: online softmax (exp2 domain), then O^T += V^T . P^T
+  // ---- per query N-tile: online softmax (exp2 domain), then O^T += V^T . P^T.
+  // The reference maximum m_run only moves when this page's maximum exceeds it by
+  // more than kRescaleLog2 (in exp2 units): until then the weights may grow up to
+  // 2^kRescaleLog2 (harmless in fp32 and bf16), and the rescale of O and l is
+  // skipped when no lane of the wave needs it.
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     float mx = s[nt][0][0];
@@ -338,10 +351,15 @@ __device__ __forceinline__ void attend_page(const unsigned char* kt, const unsig
       for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[nt][mt][i]);
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run[nt], mx);
-    const float alpha = fast_exp2((m_run[nt] - m_new) * c);
-    m_run[nt] = m_new;
-    const float nmc = -m_new * c;
+    if (__builtin_amdgcn_ballot_w64((mx - m_run[nt]) * c > kRescaleLog2) != 0) {
+      const float m_new = fmaxf(m_run[nt], mx);
+      const float alpha = fast_exp2((m_run[nt] - m_new) * c);  // 1 where m_run stays
+      m_run[nt] = m_new;
+      l_run[nt] *= alpha;
+#pragma unroll
+      for (int md = 0; md < 4; ++md) o[nt][md] *= alpha;
+    }
+    const float nmc = -m_run[nt] * c;
     float pr[4][4];
     float lsum = 0.f;
 #pragma unroll
@@ -351,7 +369,7 @@ __device__ __forceinline__ void attend_page(const unsigned char* kt, const unsig
         pr[mt][i] = fast_exp2(fmaf(s[nt][mt][i], c, nmc));
         lsum += pr[mt][i];
       }
-    l_run[nt] = fmaf(l_run[nt], alpha, lsum);
+    l_run[nt] += lsum;
     u32x4 pf[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
@@ -362,7 +380,6 @@ __device__ __forceinline__ void attend_page(const unsigned char* kt, const unsig
     }
 #pragma unroll
     for (int md = 0; md < 4; ++md) {
-      o[nt][md] *= alpha;
       o[nt][md] = mfma(va[md][0], pf[0], o[nt][md]);
       o[nt][md] = mfma(va[md][1], pf[1], o[nt][md]);
     }
@@ -520,6 +537,8 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
       *reinterpret_cast<u32x4*>(is_v ? smem + kOffOwnV + voff(j, u) : smem + kOffOwnK + koff(j, u)) = pack8(x);
     }
   }
+  volatile int* prog = reinterpret_cast<volatile int*>(smem + kOffProg);
+  if (tid < kWaves) prog[tid] = 0;
   // each wave's first page in flight while the workgroup synchronises
   if (cnt > 0) {
     stage_tile<false>(p.kpool + page_off(0), lds_k, doff);
@@ -550,6 +569,14 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
     const bool tail = cnt > 0 && first + kWaves * (cnt - 1) == npg - 1 && (L & (kPage - 1)) != 0;
     for (int i = 0; i < cnt; ++i) {
       const bool more = i + 1 < cnt;
+      // The two waves sharing a SIMD (w and w^4) get equal page counts, but issue
+      // arbitration favours the older one; the one that trails runs at raised
+      // priority.  Only the issue order changes, never which pages a wave owns.
+      if (lane == 0) prog[w] = i;
+      if (__builtin_amdgcn_readfirstlane(prog[w ^ 4]) > i)
+        __builtin_amdgcn_s_setprio(2);
+      else
+        __builtin_amdgcn_s_setprio(0);
       wait_vmcnt<8>();  // this page's K landed (its V may still be in flight)
       auto k_read = [&]() {
         if (more) {
@@ -571,6 +598,7 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
     }
   }
 
+  __builtin_amdgcn_s_setprio(0);
   // ---- merge the waves (fixed order) into this workgroup's partial
   float* mW = reinterpret_cast<float*>(smem + kOffMW);
   float* lW = reinterpret_cast<float*>(smem + kOffLW);
