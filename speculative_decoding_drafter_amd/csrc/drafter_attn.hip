@@ -673,50 +673,88 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
   __syncthreads();
   if (!*last) return;
 
+  // Memory round trips dominate here (agent-scope loads go past the L2), so every
+  // load is issued before the first use: the split maxima/sums first, then the
+  // first 8 splits' outputs; the weights only wait for the former (loads complete
+  // in order), and one barrier later the outputs are accumulated in split order.
   float* wts = reinterpret_cast<float*>(smem + kOffWts);
   const int S = p.S;
-  if (tid < nrows) {
+  auto ld = [](const float* q) { return __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+  constexpr int kColsPerThread = kRows / (kThreads / kD);
+  constexpr int kChunk = 8;
+  const int d = tid & (kD - 1), c0 = tid >> 6;
+  const float* po = p.part_o + static_cast<int64_t>(rg) * S * kRows * kD + d;
+  const bool wt_thread = tid < nrows;
+  const float* ml = p.part_ml + (static_cast<int64_t>(rg) * S * kRows + tid) * 2;
+  float mls[2 * kMaxSplits / 4];  // the first 16 splits' (m, l) of this thread's column
+  const int s_first = min(S, kMaxSplits / 4);
+  if (wt_thread) {
+#pragma unroll
+    for (int k = 0; k < kMaxSplits / 4; ++k)
+      if (k < s_first) {
+        mls[2 * k] = ld(ml + k * kRows * 2);
+        mls[2 * k + 1] = ld(ml + k * kRows * 2 + 1);
+      }
+  }
+  float v[kColsPerThread][kChunk];
+  auto load_chunk = [&](int s0) {
+#pragma unroll
+    for (int k = 0; k < kColsPerThread; ++k) {
+      const int col = c0 + (kThreads / kD) * k;
+#pragma unroll
+      for (int j = 0; j < kChunk; ++j)
+        v[k][j] = (col < nrows && s0 + j < S) ? ld(po + (static_cast<int64_t>(s0 + j) * kRows + col) * kD) : 0.f;
+    }
+  };
+  load_chunk(0);
+  if (wt_thread) {
+    // split weights exp2(c (m_s - M)) / sum_s l_s exp2(c (m_s - M)), in split order
+    // (the first 16 splits from registers, fully unrolled; any further ones reloaded)
     const int col = tid;
-    const float* ml = p.part_ml + (static_cast<int64_t>(rg) * S * kRows + col) * 2;
     float M = -INFINITY;
-    for (int ss = 0; ss < S; ++ss)
-      M = fmaxf(M, __hip_atomic_load(ml + ss * kRows * 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+#pragma unroll
+    for (int k = 0; k < kMaxSplits / 4; ++k)
+      if (k < s_first) M = fmaxf(M, mls[2 * k]);
+    for (int k = s_first; k < S; ++k) M = fmaxf(M, ld(ml + k * kRows * 2));
     float den = 0.f;
-    for (int ss = 0; ss < S; ++ss) {
-      const float m = __hip_atomic_load(ml + ss * kRows * 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const float l = __hip_atomic_load(ml + ss * kRows * 2 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+    for (int k = 0; k < kMaxSplits / 4; ++k)
+      if (k < s_first) {
+        const float e = (mls[2 * k] == -INFINITY) ? 0.f : fast_exp2((mls[2 * k] - M) * p.c);
+        wts[k * kRows + col] = e;
+        den = fmaf(mls[2 * k + 1], e, den);
+      }
+    for (int k = s_first; k < S; ++k) {
+      const float m = ld(ml + k * kRows * 2), l = ld(ml + k * kRows * 2 + 1);
       const float e = (m == -INFINITY) ? 0.f : fast_exp2((m - M) * p.c);
-      wts[ss * kRows + col] = e;
+      wts[k * kRows + col] = e;
       den = fmaf(l, e, den);
     }
     const float inv = 1.0f / den;
-    for (int ss = 0; ss < S; ++ss) wts[ss * kRows + col] *= inv;
+    for (int k = 0; k < S; ++k) wts[k * kRows + col] *= inv;
   }
   __syncthreads();
-  const float* po = p.part_o + static_cast<int64_t>(rg) * S * kRows * kD;
-  for (int idx = tid; idx < nrows * kD; idx += kThreads) {
-    const int col = idx >> 6, d = idx & (kD - 1);
-    const int t = col / kG, hh = col - kG * t;
-    float acc = 0.f;
-    if (t < b) {
-      const float* src = po + col * kD + d;
-      int ss = 0;
-      for (; ss + 8 <= S; ss += 8) {
-        float v[8];
+  float acc[kColsPerThread];
 #pragma unroll
-        for (int k = 0; k < 8; ++k)
-          v[k] = __hip_atomic_load(src + static_cast<int64_t>(ss + k) * kRows * kD, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
+  for (int k = 0; k < kColsPerThread; ++k) acc[k] = 0.f;
+  for (int s0 = 0; s0 < S; s0 += kChunk) {
+    if (s0 > 0) load_chunk(s0);
 #pragma unroll
-        for (int k = 0; k < 8; ++k) acc = fmaf(wts[(ss + k) * kRows + col], v[k], acc);
-      }
-      for (; ss < S; ++ss)
-        acc = fmaf(wts[ss * kRows + col],
-                   __hip_atomic_load(src + static_cast<int64_t>(ss) * kRows * kD, __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_AGENT),
-                   acc);
+    for (int k = 0; k < kColsPerThread; ++k) {
+      const int col = c0 + (kThreads / kD) * k;
+#pragma unroll
+      for (int j = 0; j < kChunk; ++j)
+        if (col < nrows && s0 + j < S) acc[k] = fmaf(wts[(s0 + j) * kRows + col], v[k][j], acc[k]);
     }
-    p.out[static_cast<int64_t>(r * T + t) * p.out_stride + (kG * g + hh) * kD + d] = to_bf16(acc);
+  }
+#pragma unroll
+  for (int k = 0; k < kColsPerThread; ++k) {
+    const int col = c0 + (kThreads / kD) * k;
+    if (col < nrows) {
+      const int t = col / kG, hh = col - kG * t;
+      const float val = (t < b) ? acc[k] : 0.f;
+      p.out[static_cast<int64_t>(r * T + t) * p.out_stride + (kG * g + hh) * kD + d] = to_bf16(val);
+    }
   }
 }
 
