@@ -88,6 +88,22 @@ def cpu_baseline(case, budget_s: float):
                       f"(fp64 numpy oracle, {n_req / R:.2f} calls' worth), {dt:.1f} s"}
 
 
+def measured_traffic(workload: int):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE runs
+    (scaled by a plain copy's counters), or None when the kernel source has changed
+    since those counters were taken or they cover another workload."""
+    import hashlib
+    try:
+        rec = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))
+        src = os.path.join(ROOT, "speculative_decoding_drafter_amd", "csrc", "drafter_attn.hip")
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != sha or rec.get("workload") != workload:
+        return None
+    return int(round(rec["traffic_bytes_per_launch"]))
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -176,7 +192,8 @@ def main():
                    "page_table_stride": case.stride, "splits": S, "pages_per_split": Ps,
                    "qknorm": case.qknorm, "kv_bytes_per_call": kv_bytes},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None if args.hot else measured_traffic(args.config),
                      "kernel": "drafter_attn_kernel<3,true,false>" if case.qknorm else "drafter_attn_kernel<3,false,false>"},
     }
     if not args.no_cpu_baseline:
