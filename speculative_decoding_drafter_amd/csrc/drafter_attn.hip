@@ -38,7 +38,8 @@ constexpr int kRows = 48;     // kG * kMaxT query rows per workgroup
 constexpr int kWaves = 8;                    // two per SIMD
 constexpr int kThreads = 64 * kWaves;
 constexpr int kMaxSplits = 64;
-constexpr int kMaxStride = 16384;            // pages per request row: keeps pages per wave <= 32
+constexpr int kMaxStride = 16384;            // pages per request row (with 64 splits: <= 256 per split)
+constexpr int kMaxPagesPerSplit = 64 * kWaves;  // a wave's page ids fit one 64-lane VGPR
 constexpr int kTileBytes = kPage * kD * 2;   // one [64][64] bf16 tile, 8 KiB
 constexpr int kStageBytes = 2 * kTileBytes;  // a wave's K slot then V slot
 constexpr float kRescaleLog2 = 8.0f;         // lazy-rescale headroom (exp2 units)
@@ -446,7 +447,17 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
   const int nrows = kG * T;
   const int rg = r * p.Hkv + g;
 
-  // ---- a1: lengths (device values, clamped into the contract)
+  // ---- a1: lengths and page ids.  The page ids of this wave's pages of the split
+  // (pbeg+w, pbeg+w+8, ... -- at most 64, so one VGPR holds them and the page loop
+  // reads them with readlane, with no memory access of its own) are loaded for the
+  // whole split range of the row before the length is known; only the first cnt
+  // are used, checked and clamped.
+  const int pbeg = s * p.Ps;
+  const int first = pbeg + w;
+  const int row_end = min(pbeg + p.Ps, p.pt_stride);
+  const int cand = first < row_end ? (row_end - first + kWaves - 1) / kWaves : 0;
+  int id = 0;
+  if (lane < cand) id = p.page_table[static_cast<int64_t>(r) * p.pt_stride + first + kWaves * lane];
   int L = p.ctx_lens[r];
   const int maxL = p.pt_stride * kPage;
   if (L < 0 || L > maxL) {
@@ -462,24 +473,14 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
     }
   }
   const int npg = (L + kPage - 1) / kPage;
-  const int pbeg = s * p.Ps;
   const int pend = min(npg, pbeg + p.Ps);
   const bool own = (s == p.S - 1);
   // the block's own keys go to a wave with the fewest pages of this split
   const int own_wave = max(0, pend - pbeg) & (kWaves - 1);
-
-  // This wave's pages are pbeg+w, pbeg+w+8, ... (< pend): at most 32 of them (the
-  // plan keeps pages_per_split <= 256), so one VGPR holds every page id and the
-  // page loop reads them with readlane, with no memory access of its own.
-  const int first = pbeg + w;
   const int cnt = first < pend ? (pend - first + kWaves - 1) / kWaves : 0;
-  int id = 0;
-  if (lane < cnt) {
-    id = p.page_table[static_cast<int64_t>(r) * p.pt_stride + first + kWaves * lane];
-    if (id < 0 || id >= p.num_pages) {
-      flag(p.status, DA_FLAG_PAGE_ID);
-      id = id < 0 ? 0 : p.num_pages - 1;
-    }
+  if (lane < cnt && (id < 0 || id >= p.num_pages)) {
+    flag(p.status, DA_FLAG_PAGE_ID);
+    id = id < 0 ? 0 : p.num_pages - 1;
   }
   const int64_t head_off = static_cast<int64_t>(g) * kPage * kD;
   unsigned char* kslot = smem + kOffStage + w * kStageBytes;
@@ -490,6 +491,12 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
     return static_cast<int64_t>(__builtin_amdgcn_readlane(id, i)) * p.page_stride + head_off;
   };
   const DmaOffsets doff = dma_offsets(lane);
+  // each wave's first page is in flight during the whole prologue (its slots are
+  // not touched by the prologue)
+  if (cnt > 0) {
+    stage_tile<false>(p.kpool + page_off(0), lds_k, doff);
+    stage_tile<true>(p.vpool + page_off(0), lds_v, doff);
+  }
 
   float2* cs = reinterpret_cast<float2*>(smem + kOffCS);
   // ---- a2/a3 (qknorm): rotation table, one (token, frequency) per thread
@@ -539,11 +546,6 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
   }
   volatile int* prog = reinterpret_cast<volatile int*>(smem + kOffProg);
   if (tid < kWaves) prog[tid] = 0;
-  // each wave's first page in flight while the workgroup synchronises
-  if (cnt > 0) {
-    stage_tile<false>(p.kpool + page_off(0), lds_k, doff);
-    stage_tile<true>(p.vpool + page_off(0), lds_v, doff);
-  }
   __syncthreads();
 
   const unsigned char* qt = smem + kOffQ;
@@ -630,6 +632,29 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
     }
   }
   __syncthreads();
+  if (p.S == 1) {
+    // a single split: its merged state is the answer (no partial, no combine)
+    for (int idx = tid; idx < nrows * kD; idx += kThreads) {
+      const int col = idx >> 6, d = idx & (kD - 1);
+      const int t = col / kG, hh = col - kG * t;
+      float val = 0.f;
+      if (t < b) {
+        float M = mW[col];
+#pragma unroll
+        for (int ww = 1; ww < kWaves; ++ww) M = fmaxf(M, mW[ww * kRows + col]);
+        float Ls = 0.f, acc = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < kWaves; ++ww) {
+          const float mw = mW[ww * kRows + col];
+          Ls += (mw == -INFINITY) ? 0.f : lW[ww * kRows + col] * fast_exp2((mw - M) * p.c);
+          acc += obuf[(ww * kRows + col) * kObufStride + d];
+        }
+        val = acc / Ls;
+      }
+      p.out[static_cast<int64_t>(r * T + t) * p.out_stride + (kG * g + hh) * kD + d] = to_bf16(val);
+    }
+    return;
+  }
   // The partial is published with agent-scope stores (coherent across the XCDs'
   // L2s without a cache write-back), completed before the counter increment; the
   // last workgroup reads it back with agent-scope loads.
@@ -775,22 +800,22 @@ struct Plan {
 
 // Split plan from host-known sizes only.  Aim for about one workgroup per
 // compute unit over the whole (request, KV head, page) space, with a page count
-// per split that is a multiple of the 4 waves once splits hold more than a few
-// pages; at most kMaxSplits splits.
+// per split that is a multiple of the 8 waves (small problems get fewer, fuller
+// workgroups rather than workgroups of idle waves); at most kMaxSplits splits.
 Plan make_plan(int R, int Hkv, int stride) {
   constexpr int kTargetWorkgroups = 256;
   if (stride <= 0) return {1, 1};
   const int64_t units = static_cast<int64_t>(R) * Hkv * stride;
   int ps = static_cast<int>((units + kTargetWorkgroups - 1) / kTargetWorkgroups);
-  if (ps < 1) ps = 1;
-  if (ps > kWaves) ps = (ps + kWaves - 1) / kWaves * kWaves;
+  ps = (ps + kWaves - 1) / kWaves * kWaves;  // >= one page per wave, a multiple of the waves
+  if (ps > kMaxPagesPerSplit) ps = kMaxPagesPerSplit;
   int S = (stride + ps - 1) / ps;
   if (S > kMaxSplits) {
     ps = (stride + kMaxSplits - 1) / kMaxSplits;
     ps = (ps + kWaves - 1) / kWaves * kWaves;
     S = (stride + ps - 1) / ps;
   }
-  return {S, ps};
+  return {S, ps};  // S <= 64, ps <= 512 (kMaxStride <= 64 * 256)
 }
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }

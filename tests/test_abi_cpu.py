@@ -77,6 +77,18 @@ def test_plan_covers_the_row_and_is_data_independent(lib):
                 assert s.value * p.value >= stride
                 assert (s.value - 1) * p.value < max(stride, 1)   # no split is entirely past the row
     assert lib.drafter_attn_plan(0, 1, 4, None, None) == DA_EINVAL
+    assert lib.drafter_attn_plan(1, 1, 16385, None, None) == DA_EINVAL
+
+
+def test_plan_keeps_a_waves_page_ids_in_one_register(lib):
+    # a wave owns every 8th page of its split: at most 64 of them (one id per lane)
+    for R in (1, 2, 8):
+        for hkv in (1, 2, 4, 8, 16):
+            for stride in (1, 7, 64, 511, 512, 2048, 4096, 8191, 16384):
+                s, p = ctypes.c_int32(), ctypes.c_int32()
+                assert lib.drafter_attn_plan(R, hkv, stride, ctypes.byref(s), ctypes.byref(p)) == DA_OK
+                assert -(-p.value // 8) <= 64, (R, hkv, stride, s.value, p.value)
+                assert s.value <= 64 and s.value * p.value >= stride
 
 
 def _call(lib, **over):

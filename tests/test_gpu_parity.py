@@ -183,6 +183,15 @@ def test_max_context_many_splits():
     check(to_np(run(case)), reference(case), "maxctx")
 
 
+def test_large_stride_caps_pages_per_split():
+    # 8 x 4 heads with a 4096-page row stride: the plan caps a split at 512 pages
+    # (64 per wave); one request uses the whole row, the others are short
+    lens = [4096 * 64, 3, 0, 700, 64, 65, 1, 2041]
+    case = ds.make_case(8, 8, 24, 4, lens, seed=91, stride=4096, qknorm=True, pos_dtype=torch.int64)
+    say("large stride")
+    check(to_np(run(case)), reference(case), "stride4096")
+
+
 def test_status_flags_and_clamping():
     # device-value contract breaks are clamped (no out-of-range reads) and reported
     case = ds.make_case(2, 2, 6, 1, [100, 50], seed=5, stride=2, pool_pages=4)
