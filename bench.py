@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--cpu-budget-s", type=float, default=10.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 512 MiB device copy (for counter calibration)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU run: turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, WRITE_SIZE) of a "
+                         "--calibrate-copy run into profiles/traffic.json")
     return ap.parse_args()
 
 
@@ -104,8 +107,49 @@ def measured_traffic(workload: int):
     return int(round(rec["traffic_bytes_per_launch"]))
 
 
+COPY_BYTES = 1 << 29  # the --calibrate-copy buffer
+
+
+def counter_means(path: str, counter: str):
+    """Mean counter value (KiB) per dispatch, by kernel name, from a rocprofv3 counter CSV.
+    The copy kernel is kept only for the dispatches of the 512 MiB calibration copy
+    (the largest grid of that kernel)."""
+    import csv
+    rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+    copy = [r for r in rows if "copyBuffer" in r["Kernel_Name"]]
+    big = max(int(r["Grid_Size"]) for r in copy) if copy else 0
+    out = {}
+    for r in rows:
+        if "copyBuffer" in r["Kernel_Name"] and int(r["Grid_Size"]) != big:
+            continue
+        out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return {k: (sum(v) / len(v), len(v)) for k, v in out.items()}
+
+
+def write_traffic(fetch_csv: str, write_csv: str, workload: int):
+    import hashlib
+    fetch, write = counter_means(fetch_csv, "FETCH_SIZE"), counter_means(write_csv, "WRITE_SIZE")
+    copy = next(k for k in fetch if "copyBuffer" in k)
+    kern = next(k for k in fetch if "drafter_attn_kernel<" in k)
+    fs = COPY_BYTES / 1024 / fetch[copy][0]
+    ws = COPY_BYTES / 1024 / write[copy][0]
+    src = os.path.join(ROOT, "speculative_decoding_drafter_amd", "csrc", "drafter_attn.hip")
+    rec = {"source_sha256": hashlib.sha256(open(src, "rb").read()).hexdigest(), "workload": workload,
+           "kernel": kern, "dispatches": fetch[kern][1],
+           "fetch_kib": fetch[kern][0], "write_kib": write[kern][0],
+           "copy_fetch_kib": fetch[copy][0], "copy_write_kib": write[copy][0],
+           "fetch_scale": fs, "write_scale": ws,
+           "traffic_bytes_per_launch": 1024 * (fetch[kern][0] * fs + write[kern][0] * ws)}
+    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec, indent=1))
+
+
 def main():
     args = parse()
+    if args.traffic_from:
+        write_traffic(*args.traffic_from, args.config)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this hot path is not sharded across GPUs "
               "(see the design notes); run with --gpus 1", file=sys.stderr)
