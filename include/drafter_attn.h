@@ -69,7 +69,8 @@ typedef enum da_status {
   DA_OK = 0,
   DA_EINVAL = -1,        /* an argument is outside the contract */
   DA_EUNSUPPORTED = -2,  /* head_dim / page_size / GQA ratio other than 64 / 64 / 6 */
-  DA_EWORKSPACE = -3,    /* workspace missing or smaller than drafter_attn_workspace_bytes() */
+  DA_EWORKSPACE = -3,    /* workspace missing, not 256-byte aligned, or smaller than
+                            drafter_attn_workspace_bytes() */
   DA_ELAUNCH = -4        /* the HIP runtime refused the launch (no device, bad stream, ...) */
 } da_status;
 
@@ -94,9 +95,10 @@ enum {
  * Bytes of workspace a call with these sizes needs (0 for arguments outside the
  * contract).  The workspace holds one fp32 partial (running max, weight sum,
  * unnormalised output) per (request, KV head, context split) and one counter
- * per (request, KV head).  The counters must be zero before the first call on
- * a workspace (zero the whole buffer once after allocating it); every call
- * leaves them zero again.  Two calls in flight on one workspace race.
+ * per (request, KV head).  The workspace must be 256-byte aligned (as hipMalloc
+ * returns).  The counters must be zero before the first call on a workspace
+ * (zero the whole buffer once after allocating it); every call leaves them zero
+ * again.  Two calls in flight on one workspace race.
  */
 size_t drafter_attn_workspace_bytes(int32_t num_requests, int32_t tokens_per_block,
                                     int32_t num_q_heads, int32_t num_kv_heads,

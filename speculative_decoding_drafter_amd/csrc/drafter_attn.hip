@@ -49,21 +49,19 @@ constexpr int kOffQ = 0;                                   // [48][64] bf16 quer
 constexpr int kOffCS = kOffQ + kRows * kD * 2;             // [8][32] (cos, sin) fp32
 constexpr int kOffOwnK = kOffCS + kMaxT * 32 * 8;          // own block's K rows (8 x 128 B)
 constexpr int kOffOwnV = kOffOwnK + kMaxT * kD * 2;        // own block's V rows (8 x 128 B)
-constexpr int kOffMW = kOffOwnV + kMaxT * kD * 2;          // [8][48] per-wave running max
-constexpr int kOffLW = kOffMW + kWaves * kRows * 4;        // [8][48] per-wave weight sum
+constexpr int kOffMW = kOffOwnV + kMaxT * kD * 2;          // [48][8] per-wave running max
+constexpr int kOffLW = kOffMW + kWaves * kRows * 4;        // [48][8] per-wave weight sum
 constexpr int kOffFlag = kOffLW + kWaves * kRows * 4;      // last-workgroup flag
 constexpr int kOffProg = kOffFlag + 16;                    // [8] pages done per wave
 constexpr int kOffStage = 14336;                           // [8 waves][K | V] page slots
-constexpr int kObufStride = kD + 4;                        // fp32 row stride (pad: no bank conflicts)
-constexpr int kOffObuf = kOffStage;                        // [8][48][68] fp32 merge buffer (after the loop)
-constexpr int kOffWts = kOffStage;                         // [kMaxSplits][48] fp32 combine weights
+constexpr int kObufStride = kD + 4;  // after the loop a wave's slot holds its [48][68] fp32 output (pad: no bank conflicts)
 constexpr int kSmemBytes = kOffStage + kWaves * kStageBytes;
 static_assert(kOffProg + 4 * kWaves <= kOffStage, "LDS layout");
 // the own-block tiles are read like full 64-row tiles (rows past the block are
 // masked): their 8 KiB read windows must stay inside the allocation
 static_assert(kOffOwnV + kTileBytes <= kSmemBytes, "own-block read window");
-static_assert(kWaves * kRows * kObufStride * 4 <= kWaves * kStageBytes, "merge buffer fits");
-static_assert(kMaxSplits * kRows * 4 <= kWaves * kStageBytes, "combine weights fit");
+static_assert(kRows * kObufStride * 4 <= kStageBytes, "a wave's output fits its page slot");
+static_assert(kOffMW % 16 == 0 && kOffLW % 16 == 0, "row statistics are read 16 bytes at a time");
 static_assert(kSmemBytes <= 160 * 1024, "gfx950 LDS budget");
 
 typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
@@ -72,6 +70,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 struct Params {
   const uint16_t* qkv;
@@ -166,6 +165,27 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// Device-scope 8/16-byte global accesses through a buffer resource: cache policy
+// sc1 keeps them coherent across the XCDs' L2s, and the compiler tracks their
+// completion like any other load.  Offsets past `bytes` are dropped (stores) or
+// read as zero (loads) by the hardware's range check.
+constexpr int kDeviceCoherent = 16;  // buffer cache-policy operand: sc1
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t dev_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000 /* 32-bit data format */);
+}
+__device__ __forceinline__ void st_dev_b128(__amdgpu_buffer_rsrc_t r, int off, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kDeviceCoherent);
+}
+__device__ __forceinline__ void st_dev_b64(__amdgpu_buffer_rsrc_t r, int off, f32x2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, off, 0, kDeviceCoherent);
+}
+__device__ __forceinline__ f32x4 ld_dev_b128(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kDeviceCoherent));
+}
+__device__ __forceinline__ f32x2 ld_dev_b64(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kDeviceCoherent));
 }
 
 // every LDS read this wave issued has returned: its slot may be refilled by DMA
@@ -601,8 +621,11 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
   }
 
   __builtin_amdgcn_s_setprio(0);
-  // ---- merge the waves (fixed order) into this workgroup's partial
-  float* mW = reinterpret_cast<float*>(smem + kOffMW);
+  // ---- merge the waves (fixed order).  Each wave leaves its running maxima and
+  // sums and its unnormalised output in LDS -- the output inside its own page
+  // slot, which it no longer reads -- and after one barrier each thread owns one
+  // (query row, 8 dims) of the workgroup's merged state.
+  float* mW = reinterpret_cast<float*>(smem + kOffMW);  // [48 rows][8 waves]
   float* lW = reinterpret_cast<float*>(smem + kOffLW);
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
@@ -612,81 +635,83 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
   if (lane < 16) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      mW[w * kRows + 16 * nt + lane] = m_run[nt];
-      lW[w * kRows + 16 * nt + lane] = l_run[nt];
+      mW[(16 * nt + lane) * kWaves + w] = m_run[nt];
+      lW[(16 * nt + lane) * kWaves + w] = l_run[nt];
     }
   }
-  __syncthreads();  // also: every wave is done with its page slots
-  float* obuf = reinterpret_cast<float*>(smem + kOffObuf);
+  {
+    float* ob = reinterpret_cast<float*>(kslot);  // [48][kObufStride] fp32
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int col = 16 * nt + (lane & 15);
-    float M = mW[col];
+    for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-    for (int ww = 1; ww < kWaves; ++ww) M = fmaxf(M, mW[ww * kRows + col]);
-    const float f = (m_run[nt] == -INFINITY) ? 0.f : fast_exp2((m_run[nt] - M) * p.c);
-#pragma unroll
-    for (int md = 0; md < 4; ++md) {
-      const f32x4 v = o[nt][md] * f;
-      *reinterpret_cast<f32x4*>(obuf + (w * kRows + col) * kObufStride + 16 * md + 4 * (lane >> 4)) = v;
-    }
+      for (int md = 0; md < 4; ++md)
+        *reinterpret_cast<f32x4*>(ob + (16 * nt + (lane & 15)) * kObufStride + 16 * md + 4 * (lane >> 4)) =
+            o[nt][md];
   }
   __syncthreads();
-  if (p.S == 1) {
-    // a single split: its merged state is the answer (no partial, no combine)
-    for (int idx = tid; idx < nrows * kD; idx += kThreads) {
-      const int col = idx >> 6, d = idx & (kD - 1);
-      const int t = col / kG, hh = col - kG * t;
-      float val = 0.f;
-      if (t < b) {
-        float M = mW[col];
+
+  const int row = tid >> 3, oc = tid & 7;  // query row (6t + h) and dims 8*oc .. 8*oc+7
+  const bool row_thread = row < nrows;
+  float acc[8];
+  float m_wg = -INFINITY, l_wg = 0.f;
 #pragma unroll
-        for (int ww = 1; ww < kWaves; ++ww) M = fmaxf(M, mW[ww * kRows + col]);
-        float Ls = 0.f, acc = 0.f;
+  for (int j = 0; j < 8; ++j) acc[j] = 0.f;
+  if (row_thread) {
+    const f32x4 m0 = *reinterpret_cast<const f32x4*>(mW + row * kWaves);
+    const f32x4 m1 = *reinterpret_cast<const f32x4*>(mW + row * kWaves + 4);
+    const f32x4 l0 = *reinterpret_cast<const f32x4*>(lW + row * kWaves);
+    const f32x4 l1 = *reinterpret_cast<const f32x4*>(lW + row * kWaves + 4);
+    const float mw[kWaves] = {m0[0], m0[1], m0[2], m0[3], m1[0], m1[1], m1[2], m1[3]};
+    const float lw[kWaves] = {l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
 #pragma unroll
-        for (int ww = 0; ww < kWaves; ++ww) {
-          const float mw = mW[ww * kRows + col];
-          Ls += (mw == -INFINITY) ? 0.f : lW[ww * kRows + col] * fast_exp2((mw - M) * p.c);
-          acc += obuf[(ww * kRows + col) * kObufStride + d];
-        }
-        val = acc / Ls;
+    for (int ww = 0; ww < kWaves; ++ww) m_wg = fmaxf(m_wg, mw[ww]);
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) {
+      // a wave that saw no key has m = -inf, l = 0, o = 0: weight 0
+      const float e = (mw[ww] == -INFINITY) ? 0.f : fast_exp2((mw[ww] - m_wg) * p.c);
+      l_wg = fmaf(lw[ww], e, l_wg);
+      const float* src = reinterpret_cast<const float*>(smem + kOffStage + ww * kStageBytes) +
+                         row * kObufStride + 8 * oc;
+      const f32x4 a = *reinterpret_cast<const f32x4*>(src);
+      const f32x4 c4 = *reinterpret_cast<const f32x4*>(src + 4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[j] = fmaf(e, a[j], acc[j]);
+        acc[4 + j] = fmaf(e, c4[j], acc[4 + j]);
       }
-      p.out[static_cast<int64_t>(r * T + t) * p.out_stride + (kG * g + hh) * kD + d] = to_bf16(val);
+    }
+  }
+  const int t_row = row / kG;
+  uint16_t* out_row = p.out + static_cast<int64_t>(r * T + t_row) * p.out_stride + (kG * g + row - kG * t_row) * kD +
+                      8 * oc;
+  if (p.S == 1) {
+    // a single split: its merged state is the answer (the block's own keys are
+    // in it, so l_wg > 0)
+    if (row_thread) {
+      float x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = (t_row < b) ? acc[j] / l_wg : 0.f;
+      *reinterpret_cast<u32x4*>(out_row) = pack8(x);
     }
     return;
   }
-  // The partial is published with agent-scope stores (coherent across the XCDs'
-  // L2s without a cache write-back), completed before the counter increment; the
-  // last workgroup reads it back with agent-scope loads.
+  // The partial is published with device-scope stores (coherent across the
+  // XCDs' L2s without a cache write-back), completed before the counter
+  // increment; the last workgroup reads it back with device-scope loads.
   const int rgs = rg * p.S + s;
-  {
-    float* po = p.part_o + static_cast<int64_t>(rgs) * kRows * kD;
-    for (int idx = tid; idx < 16 * NT * kD; idx += kThreads) {
-      const int col = idx >> 6, d = idx & (kD - 1);
-      float acc = obuf[col * kObufStride + d];
-#pragma unroll
-      for (int ww = 1; ww < kWaves; ++ww) acc += obuf[(ww * kRows + col) * kObufStride + d];
-      __hip_atomic_store(po + idx, acc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    if (tid < 16 * NT) {
-      const int col = tid;
-      float M = mW[col];
-#pragma unroll
-      for (int ww = 1; ww < kWaves; ++ww) M = fmaxf(M, mW[ww * kRows + col]);
-      float Ls = 0.f;
-#pragma unroll
-      for (int ww = 0; ww < kWaves; ++ww) {
-        const float mw = mW[ww * kRows + col];
-        Ls += (mw == -INFINITY) ? 0.f : lW[ww * kRows + col] * fast_exp2((mw - M) * p.c);
-      }
-      float* pm = p.part_ml + (static_cast<int64_t>(rgs) * kRows + col) * 2;
-      __hip_atomic_store(pm, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(pm + 1, Ls, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (row_thread) {
+    const __amdgpu_buffer_rsrc_t po = dev_rsrc(p.part_o + static_cast<int64_t>(rgs) * kRows * kD, kRows * kD * 4);
+    const int off = (row * kD + 8 * oc) * 4;
+    st_dev_b128(po, off, f32x4{acc[0], acc[1], acc[2], acc[3]});
+    st_dev_b128(po, off + 16, f32x4{acc[4], acc[5], acc[6], acc[7]});
+    if (oc == 0) {
+      const __amdgpu_buffer_rsrc_t pm = dev_rsrc(p.part_ml + static_cast<int64_t>(rgs) * kRows * 2, kRows * 2 * 4);
+      st_dev_b64(pm, row * 8, f32x2{m_wg, l_wg});
     }
   }
 
   // ---- a11/a12: the last workgroup of (r, g) merges the splits
-  wait_vmcnt<0>();  // this thread's partial stores are complete (visible at agent scope)
+  wait_vmcnt<0>();  // this thread's partial stores are complete (visible at device scope)
   __syncthreads();
   int* last = reinterpret_cast<int*>(smem + kOffFlag);
   if (tid == 0) {
@@ -696,91 +721,57 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
     *last = is_last;
   }
   __syncthreads();
-  if (!*last) return;
+  if (!*last || !row_thread) return;
 
-  // Memory round trips dominate here (agent-scope loads go past the L2), so every
-  // load is issued before the first use: the split maxima/sums first, then the
-  // first 8 splits' outputs; the weights only wait for the former (loads complete
-  // in order), and one barrier later the outputs are accumulated in split order.
-  float* wts = reinterpret_cast<float*>(smem + kOffWts);
+  // Thread (row, oc) merges its row's S partials in split order.  Memory round
+  // trips dominate here, so every load of a chunk of splits is issued before its
+  // first use: one round trip when S <= kChunk.
   const int S = p.S;
-  auto ld = [](const float* q) { return __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
-  constexpr int kColsPerThread = kRows / (kThreads / kD);
+  const __amdgpu_buffer_rsrc_t pm = dev_rsrc(p.part_ml + static_cast<int64_t>(rg) * S * kRows * 2, S * kRows * 2 * 4);
+  const __amdgpu_buffer_rsrc_t po = dev_rsrc(p.part_o + static_cast<int64_t>(rg) * S * kRows * kD, S * kRows * kD * 4);
   constexpr int kChunk = 8;
-  const int d = tid & (kD - 1), c0 = tid >> 6;
-  const float* po = p.part_o + static_cast<int64_t>(rg) * S * kRows * kD + d;
-  const bool wt_thread = tid < nrows;
-  const float* ml = p.part_ml + (static_cast<int64_t>(rg) * S * kRows + tid) * 2;
-  float mls[2 * kMaxSplits / 4];  // the first 16 splits' (m, l) of this thread's column
-  const int s_first = min(S, kMaxSplits / 4);
-  if (wt_thread) {
-#pragma unroll
-    for (int k = 0; k < kMaxSplits / 4; ++k)
-      if (k < s_first) {
-        mls[2 * k] = ld(ml + k * kRows * 2);
-        mls[2 * k + 1] = ld(ml + k * kRows * 2 + 1);
-      }
-  }
-  float v[kColsPerThread][kChunk];
+  f32x2 ml[kChunk];
+  f32x4 ov[kChunk][2];
   auto load_chunk = [&](int s0) {
 #pragma unroll
-    for (int k = 0; k < kColsPerThread; ++k) {
-      const int col = c0 + (kThreads / kD) * k;
-#pragma unroll
-      for (int j = 0; j < kChunk; ++j)
-        v[k][j] = (col < nrows && s0 + j < S) ? ld(po + (static_cast<int64_t>(s0 + j) * kRows + col) * kD) : 0.f;
+    for (int j = 0; j < kChunk; ++j) {
+      ml[j] = f32x2{-INFINITY, 0.f};
+      ov[j][0] = ov[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (s0 + j < S) {
+        const int prow = (s0 + j) * kRows + row;
+        ml[j] = ld_dev_b64(pm, prow * 8);
+        ov[j][0] = ld_dev_b128(po, (prow * kD + 8 * oc) * 4);
+        ov[j][1] = ld_dev_b128(po, (prow * kD + 8 * oc) * 4 + 16);
+      }
     }
   };
   load_chunk(0);
-  if (wt_thread) {
-    // split weights exp2(c (m_s - M)) / sum_s l_s exp2(c (m_s - M)), in split order
-    // (the first 16 splits from registers, fully unrolled; any further ones reloaded)
-    const int col = tid;
-    float M = -INFINITY;
+  float m_all = -INFINITY;
 #pragma unroll
-    for (int k = 0; k < kMaxSplits / 4; ++k)
-      if (k < s_first) M = fmaxf(M, mls[2 * k]);
-    for (int k = s_first; k < S; ++k) M = fmaxf(M, ld(ml + k * kRows * 2));
-    float den = 0.f;
+  for (int j = 0; j < kChunk; ++j) m_all = fmaxf(m_all, ml[j][0]);
+  for (int k = kChunk; k < S; ++k) m_all = fmaxf(m_all, ld_dev_b64(pm, (k * kRows + row) * 8)[0]);
+  float den = 0.f;
 #pragma unroll
-    for (int k = 0; k < kMaxSplits / 4; ++k)
-      if (k < s_first) {
-        const float e = (mls[2 * k] == -INFINITY) ? 0.f : fast_exp2((mls[2 * k] - M) * p.c);
-        wts[k * kRows + col] = e;
-        den = fmaf(mls[2 * k + 1], e, den);
-      }
-    for (int k = s_first; k < S; ++k) {
-      const float m = ld(ml + k * kRows * 2), l = ld(ml + k * kRows * 2 + 1);
-      const float e = (m == -INFINITY) ? 0.f : fast_exp2((m - M) * p.c);
-      wts[k * kRows + col] = e;
-      den = fmaf(l, e, den);
-    }
-    const float inv = 1.0f / den;
-    for (int k = 0; k < S; ++k) wts[k * kRows + col] *= inv;
-  }
-  __syncthreads();
-  float acc[kColsPerThread];
-#pragma unroll
-  for (int k = 0; k < kColsPerThread; ++k) acc[k] = 0.f;
+  for (int j = 0; j < 8; ++j) acc[j] = 0.f;
   for (int s0 = 0; s0 < S; s0 += kChunk) {
     if (s0 > 0) load_chunk(s0);
 #pragma unroll
-    for (int k = 0; k < kColsPerThread; ++k) {
-      const int col = c0 + (kThreads / kD) * k;
+    for (int j = 0; j < kChunk; ++j) {
+      // split weight exp2(c (m_s - M)); a split that saw no key (m = -inf) has weight 0
+      const float e = (ml[j][0] == -INFINITY) ? 0.f : fast_exp2((ml[j][0] - m_all) * p.c);
+      den = fmaf(ml[j][1], e, den);
 #pragma unroll
-      for (int j = 0; j < kChunk; ++j)
-        if (col < nrows && s0 + j < S) acc[k] = fmaf(wts[(s0 + j) * kRows + col], v[k][j], acc[k]);
+      for (int q = 0; q < 4; ++q) {
+        acc[q] = fmaf(e, ov[j][0][q], acc[q]);
+        acc[4 + q] = fmaf(e, ov[j][1][q], acc[4 + q]);
+      }
     }
   }
+  // den > 0: the last split holds the block's own keys
+  float x[8];
 #pragma unroll
-  for (int k = 0; k < kColsPerThread; ++k) {
-    const int col = c0 + (kThreads / kD) * k;
-    if (col < nrows) {
-      const int t = col / kG, hh = col - kG * t;
-      const float val = (t < b) ? acc[k] : 0.f;
-      p.out[static_cast<int64_t>(r * T + t) * p.out_stride + (kG * g + hh) * kD + d] = to_bf16(val);
-    }
-  }
+  for (int j = 0; j < 8; ++j) x[j] = (t_row < b) ? acc[j] / den : 0.f;
+  *reinterpret_cast<u32x4*>(out_row) = pack8(x);
 }
 
 // ---------------------------------------------------------------------------------
@@ -896,6 +887,7 @@ int validate(const Common& a, size_t need_ws) {
   if (!(std::isfinite(a.scale) && a.scale > 0.f)) return fail(DA_EINVAL, "scale must be finite and > 0");
   if (!a.workspace || a.workspace_bytes < need_ws)
     return fail(DA_EWORKSPACE, "workspace missing or smaller than drafter_attn_workspace_bytes()");
+  if (reinterpret_cast<uintptr_t>(a.workspace) & 255u) return fail(DA_EWORKSPACE, "workspace must be 256-byte aligned");
   // aliasing: out must not overlap any input or the workspace; the workspace no input
   const int64_t rows = static_cast<int64_t>(a.R) * a.T;
   const size_t out_n = static_cast<size_t>(((rows - 1) * a.out_row_stride + a.Hq * kD) * 2);

@@ -134,6 +134,7 @@ def _call(lib, **over):
     (dict(scale=float("nan")), DA_EINVAL),
     (dict(workspace=None), DA_EWORKSPACE),
     (dict(workspace_bytes=64), DA_EWORKSPACE),
+    (dict(workspace=0xA00000 + 16), DA_EWORKSPACE),  # not 256-byte aligned
     (dict(out=0x10000 + 256), DA_EINVAL),  # out overlaps qkv
     (dict(out=0x200000), DA_EINVAL),       # out overlaps the pool
     (dict(workspace=0x200000), DA_EINVAL), # workspace overlaps the pool
