@@ -412,9 +412,9 @@ __device__ __forceinline__ void flag(int32_t* status, int bit) {
 }
 
 // One 64-value head row held by 8 lanes (8 values each, lane u has dims 8u..8u+7):
-// RMSNorm with weight w, then NeoX rotation with the (cos, sin) row `cs`.
-__device__ __forceinline__ void norm_rope_row(float (&x)[8], const uint16_t* w, float eps,
-                                              const float2* cs, int u) {
+// RMSNorm with the weights' 8 bf16 values `wr` for those dims, then NeoX rotation
+// with the (cos, sin) row `cs`.
+__device__ __forceinline__ void norm_rope_row(float (&x)[8], u32x4 wr, float eps, const float2* cs, int u) {
   float ss = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
@@ -422,7 +422,6 @@ __device__ __forceinline__ void norm_rope_row(float (&x)[8], const uint16_t* w, 
   ss += __shfl_xor(ss, 2);
   ss += __shfl_xor(ss, 4);
   const float inv = 1.0f / sqrtf(ss * (1.0f / kD) + eps);
-  const u32x4 wr = ld16(w + 8 * u);
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const float we = (e & 1) ? bf_hi(wr[e >> 1]) : bf_lo(wr[e >> 1]);
@@ -467,34 +466,63 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
   const int nrows = kG * T;
   const int rg = r * p.Hkv + g;
 
-  // ---- a1: lengths and page ids.  The page ids of this wave's pages of the split
-  // (pbeg+w, pbeg+w+8, ... -- at most 64, so one VGPR holds them and the page loop
-  // reads them with readlane, with no memory access of its own) are loaded for the
-  // whole split range of the row before the length is known; only the first cnt
-  // are used, checked and clamped.
+  // ---- a1: every global load of the prologue is issued first and consumed before
+  // the first page's DMA: the waits the compiler places before a use cannot tell
+  // those loads from the DMA (issued from inline asm), so a load still pending
+  // after it would make the prologue wait for the whole page.
+  //
+  // The page ids of this wave's pages of the split (pbeg+w, pbeg+w+8, ... -- at
+  // most 64, so one VGPR holds them and the page loop reads them with readlane,
+  // with no memory access of its own) are loaded for the whole split range of the
+  // row before the length is known; only the first cnt are used, checked and
+  // clamped.
   const int pbeg = s * p.Ps;
   const int first = pbeg + w;
   const int row_end = min(pbeg + p.Ps, p.pt_stride);
   const int cand = first < row_end ? (row_end - first + kWaves - 1) / kWaves : 0;
   int id = 0;
   if (lane < cand) id = p.page_table[static_cast<int64_t>(r) * p.pt_stride + first + kWaves * lane];
+  const bool own = (s == p.S - 1);
+  // Thread (sub, u) holds dims 8u .. 8u+7 of one head row: query row sub = 6t + h
+  // of the tile (sub < 6T), or, in the last split, row j < T of the block's own K
+  // (sub = 48 + j) or V (sub = 56 + j).  Rows past the block length are loaded
+  // (they exist) and zeroed below.
+  const int sub = tid >> 3, u = tid & 7;
+  const int q_t = sub / kG;
+  const int oj = (sub - 48) & (kMaxT - 1);
+  const bool is_q = sub < nrows;
+  const bool own_v = sub >= 48 + kMaxT;
+  const bool is_own = own && sub >= 48 && sub < 48 + 2 * kMaxT && oj < T;
+  u32x4 raw = {0u, 0u, 0u, 0u}, wraw = {0u, 0u, 0u, 0u};
+  if (is_q) {
+    raw = ld16(p.qkv + static_cast<int64_t>(r * T + q_t) * p.qkv_stride + (kG * g + sub - kG * q_t) * kD + 8 * u);
+    if (QKNORM) wraw = ld16(p.wq + 8 * u);
+  } else if (is_own) {
+    raw = ld16(p.qkv + static_cast<int64_t>(r * T + oj) * p.qkv_stride + (own_v ? p.Hq + p.Hkv + g : p.Hq + g) * kD +
+               8 * u);
+    if (QKNORM && !own_v) wraw = ld16(p.wk + 8 * u);
+  }
+  int64_t pos = 0;
+  if (QKNORM && tid < T * 32) {
+    const int t = tid >> 5;
+    pos = POS64 ? static_cast<const int64_t*>(p.positions)[r * T + t]
+                : static_cast<int64_t>(static_cast<const int32_t*>(p.positions)[r * T + t]);
+  }
   int L = p.ctx_lens[r];
+  int b = p.blk_lens ? p.blk_lens[r] : T;
+  asm volatile("" ::"v"(raw), "v"(wraw), "v"(pos), "v"(L), "v"(b));  // every prologue load has landed
+
   const int maxL = p.pt_stride * kPage;
   if (L < 0 || L > maxL) {
     if (tid == 0 && s == 0 && g == 0) flag(p.status, DA_FLAG_CONTEXT_LEN);
     L = L < 0 ? 0 : maxL;
   }
-  int b = T;
-  if (p.blk_lens) {
-    b = p.blk_lens[r];
-    if (b < 1 || b > T) {
-      if (tid == 0 && s == 0 && g == 0) flag(p.status, DA_FLAG_BLOCK_LEN);
-      b = b < 1 ? 1 : T;
-    }
+  if (b < 1 || b > T) {
+    if (tid == 0 && s == 0 && g == 0) flag(p.status, DA_FLAG_BLOCK_LEN);
+    b = b < 1 ? 1 : T;
   }
   const int npg = (L + kPage - 1) / kPage;
   const int pend = min(npg, pbeg + p.Ps);
-  const bool own = (s == p.S - 1);
   // the block's own keys go to a wave with the fewest pages of this split
   const int own_wave = max(0, pend - pbeg) & (kWaves - 1);
   const int cnt = first < pend ? (pend - first + kWaves - 1) / kWaves : 0;
@@ -511,8 +539,8 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
     return static_cast<int64_t>(__builtin_amdgcn_readlane(id, i)) * p.page_stride + head_off;
   };
   const DmaOffsets doff = dma_offsets(lane);
-  // each wave's first page is in flight during the whole prologue (its slots are
-  // not touched by the prologue)
+  // each wave's first page is in flight during the rest of the prologue (its slots
+  // are not touched by the prologue)
   if (cnt > 0) {
     stage_tile<false>(p.kpool + page_off(0), lds_k, doff);
     stage_tile<true>(p.vpool + page_off(0), lds_v, doff);
@@ -522,9 +550,7 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
   // ---- a2/a3 (qknorm): rotation table, one (token, frequency) per thread
   if (QKNORM) {
     if (tid < T * 32) {
-      const int t = tid >> 5, i = tid & 31;
-      const int64_t pos = POS64 ? static_cast<const int64_t*>(p.positions)[r * T + t]
-                                : static_cast<int64_t>(static_cast<const int32_t*>(p.positions)[r * T + t]);
+      const int i = tid & 31;
       const double inv_freq = exp2(-static_cast<double>(i) * (1.0 / 32.0) * p.log2_base);  // base^(-2i/64)
       const double th = static_cast<double>(pos) * inv_freq;
       const double kq = rint(th * 0.15915494309189535);          // 1 / (2 pi)
@@ -536,35 +562,30 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
     __syncthreads();
   }
 
-  // ---- a4: query tile (and the own block's K/V rows) into LDS; 8 lanes per row
-  {
-    const int sub = tid >> 3, u = tid & 7;
-    unsigned char* qt = smem + kOffQ;
-    for (int n = sub; n < 16 * NT; n += kThreads / 8) {
-      const int t = n / kG;
-      float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      if (n < nrows && t < b) {
-        const int h = kG * g + (n - kG * t);
-        unpack8(ld16(p.qkv + static_cast<int64_t>(r * T + t) * p.qkv_stride + h * kD + 8 * u), x);
-        if (QKNORM) norm_rope_row(x, p.wq, p.eps, cs + t * 32, u);
-      }
-      *reinterpret_cast<u32x4*>(qt + qoff(n, u)) = pack8(x);
-    }
-    if (own && sub >= 48 && sub < 48 + 2 * kMaxT) {
-      // rows j < 8 of the own block's K (RMSNorm + RoPE in the qknorm variant) and V,
-      // laid out like staged tiles; rows past b are zero, rows past 8 are never valid
-      const int j = (sub - 48) & (kMaxT - 1);
-      const bool is_v = sub >= 48 + kMaxT;
-      float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      if (j < b) {
-        const int col = (is_v ? (p.Hq + p.Hkv + g) : (p.Hq + g)) * kD + 8 * u;
-        unpack8(ld16(p.qkv + static_cast<int64_t>(r * T + j) * p.qkv_stride + col), x);
-        if (QKNORM && !is_v) norm_rope_row(x, p.wk, p.eps, cs + j * 32, u);
-      }
-      *reinterpret_cast<u32x4*>(is_v ? smem + kOffOwnV + voff(j, u) : smem + kOffOwnK + koff(j, u)) = pack8(x);
-    }
+  // ---- a4: query tile (and the own block's K/V rows) into LDS as bf16; rows of
+  // the tile past 6T and rows past the block length are zero
+  if (sub < 16 * NT || is_own) {
+    float x[8];
+    unpack8(raw, x);
+    const int t = is_q ? q_t : oj;
+    const bool live = (is_q || is_own) && t < b;
+    if (QKNORM && live && !own_v) norm_rope_row(x, wraw, p.eps, cs + t * 32, u);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = live ? x[e] : 0.f;
+    unsigned char* dst = sub < 48 ? smem + kOffQ + qoff(sub, u)
+                                  : (own_v ? smem + kOffOwnV + voff(oj, u) : smem + kOffOwnK + koff(oj, u));
+    *reinterpret_cast<u32x4*>(dst) = pack8(x);
   }
-  volatile int* prog = reinterpret_cast<volatile int*>(smem + kOffProg);
+  if (own && sub >= 48 && sub < 48 + 2 * kMaxT && oj >= T) {
+    // own-block rows T .. 7 are never valid keys: zero
+    *reinterpret_cast<u32x4*>(own_v ? smem + kOffOwnV + voff(oj, u) : smem + kOffOwnK + koff(oj, u)) =
+        u32x4{0u, 0u, 0u, 0u};
+  }
+  // pages done per wave, read by the other wave of the SIMD.  Volatile keeps every
+  // access; the explicit LDS address space keeps them ds_read/ds_write (a generic
+  // volatile access would become a flat access that waits for the page DMA).
+  volatile __attribute__((address_space(3))) int* prog =
+      (volatile __attribute__((address_space(3))) int*)(smem + kOffProg);
   if (tid < kWaves) prog[tid] = 0;
   __syncthreads();
 
