@@ -36,6 +36,7 @@ constexpr int kG = 6;         // query heads per KV head
 constexpr int kMaxT = 8;      // tokens per block
 constexpr int kRows = 48;     // kG * kMaxT query rows per workgroup
 constexpr int kWaves = 8;                    // two per SIMD
+static_assert(8 * (kWaves - 2) >= 48, "waves kWaves-2.. hold no query rows (sub = 8w + lane/8)");
 constexpr int kThreads = 64 * kWaves;
 constexpr int kMaxSplits = 64;
 constexpr int kMaxStride = 16384;            // pages per request row (with 64 splits: <= 256 per split)
@@ -469,7 +470,7 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
   // ---- a1: every global load of the prologue is issued first and consumed before
   // the first page's DMA: the waits the compiler places before a use cannot tell
   // those loads from the DMA (issued from inline asm), so a load still pending
-  // after it would make the prologue wait for the whole page.
+  // after it would wait for the whole page.
   //
   // The page ids of this wave's pages of the split (pbeg+w, pbeg+w+8, ... -- at
   // most 64, so one VGPR holds them and the page loop reads them with readlane,
@@ -539,9 +540,8 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
     return static_cast<int64_t>(__builtin_amdgcn_readlane(id, i)) * p.page_stride + head_off;
   };
   const DmaOffsets doff = dma_offsets(lane);
-  // each wave's first page is in flight during the rest of the prologue (its slots
-  // are not touched by the prologue)
-  if (cnt > 0) {
+  const bool early_dma = w >= kWaves - 2;  // no query rows: sub = 8w + lane/8 >= 48
+  if (early_dma && cnt > 0) {
     stage_tile<false>(p.kpool + page_off(0), lds_k, doff);
     stage_tile<true>(p.vpool + page_off(0), lds_v, doff);
   }
@@ -580,6 +580,17 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
     // own-block rows T .. 7 are never valid keys: zero
     *reinterpret_cast<u32x4*>(own_v ? smem + kOffOwnV + voff(oj, u) : smem + kOffOwnK + koff(oj, u)) =
         u32x4{0u, 0u, 0u, 0u};
+  }
+  // Waves 0..5 issue their first page's DMA once their share of the prologue is
+  // done (the slots are not touched by the prologue).  A CU takes only about two
+  // waves' worth of these 1 KiB DMAs at once; a wave issuing more waits until the
+  // memory system drains, so a wave that issued before its prologue work would hold
+  // the prologue back.  Waves 6 and 7, which hold no query rows, issue theirs
+  // before the prologue: the stream starts early, and the other waves' first pages
+  // are still in flight when the page loop starts and requests the second ones.
+  if (!early_dma && cnt > 0) {
+    stage_tile<false>(p.kpool + page_off(0), lds_k, doff);
+    stage_tile<true>(p.vpool + page_off(0), lds_v, doff);
   }
   // pages done per wave, read by the other wave of the SIMD.  Volatile keeps every
   // access; the explicit LDS address space keeps them ds_read/ds_write (a generic
