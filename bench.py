@@ -4,13 +4,15 @@ Default workload: 8 requests x 8 draft tokens, 24 query / 4 KV heads, head_dim 6
 context 32768 tokens per request (512 HND pages of 64 each, 4096 pages shuffled
 across a 5000-page bf16 pool), per-head q/k RMSNorm + NeoX RoPE in the kernel.
 
-A step is one call of drafter_attn_qknorm (one kernel launch).  Inputs are
-resident in HBM before timing starts.  Before every step (warm-up and timed)
+A step is one call of drafter_attn_qknorm (one kernel launch; ``--graph`` captures
+it once in a HIP graph and replays that instead).  Inputs are resident in HBM
+before timing starts.  Before every step (warm-up and timed)
 an untimed kernel reads a 1 GiB buffer so that neither the L2 nor the 256 MB
 Infinity Cache holds the 268 MB of K/V the call reads: each timed call streams
 its pages from HBM.  (The flush only reads, so it leaves no dirty lines whose
 write-back would compete with the timed call.)  Each call is bracketed by HIP events on the
-stream it is launched on; ms_per_step is their mean.  ``--hot`` times
+stream it is launched on; ms_per_step is their mean (the median and p10/p90 are
+reported too).  ``--hot`` times
 back-to-back calls without the flush instead (reported, not the headline).
 
 value = algorithmic K/V bytes per call / mean call time (GB/s): every context
@@ -35,6 +37,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=5, choices=[1, 2, 3, 5])
     ap.add_argument("--hot", action="store_true", help="no cache flush between calls")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay one call captured in a HIP graph instead of launching it directly "
+                         "(measured ~7.6 us slower per call between the events)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=10.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -177,14 +182,25 @@ def main():
     flush = None if args.hot else torch.ones(1 << 28, dtype=torch.float32, device=dev)
     flush_out = torch.empty((), dtype=torch.float32, device=dev)
 
+    step = call
+    if args.graph:
+        # one call captured in a HIP graph (after an eager warm-up); each step replays it
+        call()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            call()
+        torch.cuda.synchronize()
+        step = graph.replay
+
     def one(timed_events=None):
         if flush is not None:
             torch.sum(flush, dim=0, out=flush_out)
         if timed_events is None:
-            call()
+            step()
         else:
             timed_events[0].record()
-            call()
+            step()
             timed_events[1].record()
 
     for _ in range(args.warmup):
@@ -212,6 +228,12 @@ def main():
     kv_bytes = case.kv_bytes()
     gbs = kv_bytes / (mean_ms * 1e-3) / 1e9
     S, Ps = plan(case.R, case.Hkv, case.stride)
+    # every byte a call moves: K/V pages, the qkv rows it reads, the output, and the
+    # split partials (written once, read back once by the combine)
+    rows = case.R * case.T
+    other_bytes = rows * (case.Hq + 2 * case.Hkv) * 64 * 2 + rows * case.Hq * 64 * 2
+    if S > 1:
+        other_bytes += 2 * case.R * case.Hkv * S * 48 * 66 * 4
     line = {
         "metric": "K/V-read HBM GB/s (% of MI355X peak) and us/call, 8 req x 8 tok, 24/4 heads",
         "value": round(gbs, 2),
@@ -223,6 +245,9 @@ def main():
         "us_per_call": round(mean_ms * 1e3, 3),
         "us_p10_p50_p90": [round(p10 * 1e3, 3), round(p50 * 1e3, 3), round(p90 * 1e3, 3)],
         "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "kv_GBs_at_median": round(kv_bytes / (p50 * 1e-3) / 1e9, 2),
+        "all_bytes_GBs": round((kv_bytes + other_bytes) / (mean_ms * 1e-3) / 1e9, 2),
+        "launch": "HIP graph replay" if args.graph else "direct",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -234,7 +259,7 @@ def main():
                    "q_heads": case.Hq, "kv_heads": case.Hkv, "head_dim": 64, "page": 64,
                    "context_lens_sum": int(case.context_lens.sum()), "pool_pages": case.num_pages,
                    "page_table_stride": case.stride, "splits": S, "pages_per_split": Ps,
-                   "qknorm": case.qknorm, "kv_bytes_per_call": kv_bytes},
+                   "qknorm": case.qknorm, "kv_bytes_per_call": kv_bytes, "other_bytes_per_call": other_bytes},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "traffic": None if args.hot else measured_traffic(args.config),

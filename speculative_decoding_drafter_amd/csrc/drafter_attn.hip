@@ -720,9 +720,10 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
     // a single split: its merged state is the answer (the block's own keys are
     // in it, so l_wg > 0)
     if (row_thread) {
+      const float inv = 1.0f / l_wg;
       float x[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) x[j] = (t_row < b) ? acc[j] / l_wg : 0.f;
+      for (int j = 0; j < 8; ++j) x[j] = (t_row < b) ? acc[j] * inv : 0.f;
       *reinterpret_cast<u32x4*>(out_row) = pack8(x);
     }
     return;
@@ -800,9 +801,10 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
     }
   }
   // den > 0: the last split holds the block's own keys
+  const float inv = 1.0f / den;
   float x[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) x[j] = (t_row < b) ? acc[j] / den : 0.f;
+  for (int j = 0; j < 8; ++j) x[j] = (t_row < b) ? acc[j] * inv : 0.f;
   *reinterpret_cast<u32x4*>(out_row) = pack8(x);
 }
 
