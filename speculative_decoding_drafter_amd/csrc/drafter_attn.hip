@@ -447,6 +447,12 @@ __device__ __forceinline__ void unpack8(u32x4 raw, float (&x)[8]) {
   }
 }
 
+// x[0..3] -> dims d..d+3 of an output row, x[4..7] -> dims d+32..d+35 (bf16)
+__device__ __forceinline__ void store_out8(uint16_t* dst, const float (&x)[8]) {
+  *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+  *reinterpret_cast<u32x2*>(dst + 32) = u32x2{pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])};
+}
+
 __device__ __forceinline__ u32x4 pack8(const float (&x)[8]) {
   u32x4 r;
 #pragma unroll
@@ -682,7 +688,10 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
   }
   __syncthreads();
 
-  const int row = tid >> 3, oc = tid & 7;  // query row (6t + h) and dims 8*oc .. 8*oc+7
+  // query row (6t + h) and dims 4*oc .. 4*oc+3 and 32+4*oc .. 32+4*oc+3: each
+  // 16-byte access of a wave's 8 threads of a row then covers one whole 128-byte
+  // line of the row (whole-line writes through the L2)
+  const int row = tid >> 3, oc = tid & 7;
   const bool row_thread = row < nrows;
   float acc[8];
   float m_wg = -INFINITY, l_wg = 0.f;
@@ -703,9 +712,9 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
       const float e = (mw[ww] == -INFINITY) ? 0.f : fast_exp2((mw[ww] - m_wg) * p.c);
       l_wg = fmaf(lw[ww], e, l_wg);
       const float* src = reinterpret_cast<const float*>(smem + kOffStage + ww * kStageBytes) +
-                         row * kObufStride + 8 * oc;
+                         row * kObufStride + 4 * oc;
       const f32x4 a = *reinterpret_cast<const f32x4*>(src);
-      const f32x4 c4 = *reinterpret_cast<const f32x4*>(src + 4);
+      const f32x4 c4 = *reinterpret_cast<const f32x4*>(src + 32);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         acc[j] = fmaf(e, a[j], acc[j]);
@@ -715,7 +724,7 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
   }
   const int t_row = row / kG;
   uint16_t* out_row = p.out + static_cast<int64_t>(r * T + t_row) * p.out_stride + (kG * g + row - kG * t_row) * kD +
-                      8 * oc;
+                      4 * oc;
   if (p.S == 1) {
     // a single split: its merged state is the answer (the block's own keys are
     // in it, so l_wg > 0)
@@ -724,7 +733,7 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
       float x[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) x[j] = (t_row < b) ? acc[j] * inv : 0.f;
-      *reinterpret_cast<u32x4*>(out_row) = pack8(x);
+      store_out8(out_row, x);
     }
     return;
   }
@@ -734,9 +743,9 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
   const int rgs = rg * p.S + s;
   if (row_thread) {
     const __amdgpu_buffer_rsrc_t po = dev_rsrc(p.part_o + static_cast<int64_t>(rgs) * kRows * kD, kRows * kD * 4);
-    const int off = (row * kD + 8 * oc) * 4;
+    const int off = (row * kD + 4 * oc) * 4;
     st_dev_b128(po, off, f32x4{acc[0], acc[1], acc[2], acc[3]});
-    st_dev_b128(po, off + 16, f32x4{acc[4], acc[5], acc[6], acc[7]});
+    st_dev_b128(po, off + 128, f32x4{acc[4], acc[5], acc[6], acc[7]});
     if (oc == 0) {
       const __amdgpu_buffer_rsrc_t pm = dev_rsrc(p.part_ml + static_cast<int64_t>(rgs) * kRows * 2, kRows * 2 * 4);
       st_dev_b64(pm, row * 8, f32x2{m_wg, l_wg});
@@ -773,8 +782,8 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
       if (s0 + j < S) {
         const int prow = (s0 + j) * kRows + row;
         ml[j] = ld_dev_b64(pm, prow * 8);
-        ov[j][0] = ld_dev_b128(po, (prow * kD + 8 * oc) * 4);
-        ov[j][1] = ld_dev_b128(po, (prow * kD + 8 * oc) * 4 + 16);
+        ov[j][0] = ld_dev_b128(po, (prow * kD + 4 * oc) * 4);
+        ov[j][1] = ld_dev_b128(po, (prow * kD + 4 * oc) * 4 + 128);
       }
     }
   };
@@ -805,7 +814,7 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
   float x[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) x[j] = (t_row < b) ? acc[j] * inv : 0.f;
-  *reinterpret_cast<u32x4*>(out_row) = pack8(x);
+  store_out8(out_row, x);
 }
 
 // ---------------------------------------------------------------------------------
