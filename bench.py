@@ -96,18 +96,31 @@ def cpu_baseline(case, budget_s: float):
                       f"(fp64 numpy oracle, {n_req / R:.2f} calls' worth), {dt:.1f} s"}
 
 
+KERNEL_SRC = os.path.join(ROOT, "speculative_decoding_drafter_amd", "csrc", "drafter_attn.hip")
+
+
+def kernel_code_hash() -> str:
+    """sha256 of the kernel source with comments removed and whitespace collapsed: any change
+    to the code changes it, an edit of a comment does not."""
+    import hashlib
+    import re
+    text = open(KERNEL_SRC).read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    text = " ".join(text.split())
+    return hashlib.sha256(text.encode()).hexdigest()
+
+
 def measured_traffic(workload: int):
     """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE runs
-    (scaled by a plain copy's counters), or None when the kernel source has changed
+    (scaled by a plain copy's counters), or None when the kernel code has changed
     since those counters were taken or they cover another workload."""
-    import hashlib
     try:
         rec = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))
-        src = os.path.join(ROOT, "speculative_decoding_drafter_amd", "csrc", "drafter_attn.hip")
-        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        sha = kernel_code_hash()
     except (OSError, ValueError):
         return None
-    if rec.get("source_sha256") != sha or rec.get("workload") != workload:
+    if rec.get("kernel_code_sha256") != sha or rec.get("workload") != workload:
         return None
     return int(round(rec["traffic_bytes_per_launch"]))
 
@@ -132,14 +145,12 @@ def counter_means(path: str, counter: str):
 
 
 def write_traffic(fetch_csv: str, write_csv: str, workload: int):
-    import hashlib
     fetch, write = counter_means(fetch_csv, "FETCH_SIZE"), counter_means(write_csv, "WRITE_SIZE")
     copy = next(k for k in fetch if "copyBuffer" in k)
     kern = next(k for k in fetch if "drafter_attn_kernel<" in k)
     fs = COPY_BYTES / 1024 / fetch[copy][0]
     ws = COPY_BYTES / 1024 / write[copy][0]
-    src = os.path.join(ROOT, "speculative_decoding_drafter_amd", "csrc", "drafter_attn.hip")
-    rec = {"source_sha256": hashlib.sha256(open(src, "rb").read()).hexdigest(), "workload": workload,
+    rec = {"kernel_code_sha256": kernel_code_hash(), "workload": workload,
            "kernel": kern, "dispatches": fetch[kern][1],
            "fetch_kib": fetch[kern][0], "write_kib": write[kern][0],
            "copy_fetch_kib": fetch[copy][0], "copy_write_kib": write[copy][0],

@@ -3,16 +3,16 @@
 // k3_drafter_attn_qknorm and their contracts).  The ABI is documented in
 // include/drafter_attn.h.
 //
-// One launch per call.  Workgroup (split s, KV head g, request r), 4 waves:
+// One launch per call.  Workgroup (split s, KV head g, request r), 8 waves:
 //   1. prologue: the 6*T query rows of group g (and, in the last split, the
 //      block's own K/V rows) go to LDS as bf16; in the qknorm variant each row
 //      is RMS-normalised and NeoX-rotated in fp32 on the way (angle in fp64).
-//   2. page loop: wave w walks pages s*Ps+w, +4, ... of the split.  Per page:
-//      K rows are loaded straight into MFMA A-fragments, S^T = K.Q^T with
-//      v_mfma_f32_16x16x32_bf16, online softmax in the exp2 domain, V is
-//      transposed through a per-wave LDS tile, O^T += V^T.P^T with MFMA.  The
-//      next page's K/V loads are in flight while the current page computes.
-//   3. the 4 waves merge (max, sum, output) through LDS and write one fp32
+//   2. page loop: wave w walks pages s*Ps+w, +8, ... of the split.  Per page:
+//      the K and V tiles are copied HBM -> LDS by DMA (global_load_lds), S^T =
+//      K.Q^T with v_mfma_f32_16x16x32_bf16, online softmax in the exp2 domain,
+//      V^T fragments by transposing LDS reads, O^T += V^T.P^T with MFMA.  The
+//      next page's DMA is in flight while the current page computes.
+//   3. the 8 waves merge (max, sum, output) through LDS and write one fp32
 //      partial per workgroup;
 //   4. the last workgroup of each (r, g) (device-scope counter, reset by that
 //      workgroup) merges the splits in fixed order and writes bf16 output.
