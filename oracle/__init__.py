@@ -13,5 +13,6 @@ from .drafter_attn_oracle import (  # noqa: F401
     drafter_attn,
     drafter_attn_qknorm,
     drafter_attn_split_merge,
+    qk_norm_rope,
     OracleContractError,
 )

@@ -243,6 +243,34 @@ def drafter_attn_qknorm(qkv, k_pool, v_pool, page_table, context_lens, block_len
                 num_kv_heads, T, scale, prep(q_norm_weight), prep(k_norm_weight), return_probs)
 
 
+def qk_norm_rope(qkv, positions, q_norm_weight, k_norm_weight, *, num_q_heads: int,
+                 num_kv_heads: int, eps: float = 1e-5, rope_base: float = 10000.0) -> np.ndarray:
+    """fused_qk_norm_rope, the drafter's cell, on packed qkv rows.
+
+    PR #20532, commit adding fused_qk_norm_rope's drafter cell (head_dim 64,
+    6 query heads per KV head, 1 to 64 tokens, eps 1e-5, base 10000, NeoX); the
+    attention commit says the qknorm variant uses that op's arithmetic.  Every
+    query head of a row is RMS-normalised with ``q_norm_weight`` and every key
+    head with ``k_norm_weight``, then NeoX-rotated at the row's position.  The
+    value heads and any columns past the heads are returned unchanged.  The
+    result is a float64 copy; the op itself works in place on bf16 rows.
+    """
+    x = np.array(qkv, dtype=np.float64, copy=True)
+    pos = np.asarray(positions, dtype=np.int64)
+    Hq, Hkv = int(num_q_heads), int(num_kv_heads)
+    if x.ndim != 2 or pos.shape != (x.shape[0],):
+        raise OracleContractError("qkv must be [N, width] with one position per row")
+    if x.shape[1] < (Hq + 2 * Hkv) * HEAD_DIM or Hkv < 1 or Hq != GQA * Hkv:
+        raise OracleContractError("qkv narrower than its heads, or not 6 query heads per KV head")
+    for h in range(Hq):
+        c = q_cols(h, Hq, Hkv)
+        x[:, c] = rope_neox(rms_norm(x[:, c], q_norm_weight, eps), pos, rope_base)
+    for g in range(Hkv):
+        c = k_cols(g, Hq, Hkv)
+        x[:, c] = rope_neox(rms_norm(x[:, c], k_norm_weight, eps), pos, rope_base)
+    return x
+
+
 def drafter_attn_split_merge(qkv, k_pool, v_pool, page_table, context_lens, block_lens=None, *,
                              num_splits: int, num_q_heads: int, num_kv_heads: int,
                              tokens_per_block: int, scale: Optional[float] = None,

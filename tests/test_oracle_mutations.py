@@ -19,6 +19,40 @@ orig_rope = mod.rope_neox
 orig_freq = mod.rope_inv_freq
 orig_gather = mod.gather_context
 orig_attend = mod._softmax_attend
+orig_qknr = mod.qk_norm_rope
+
+
+def _qknr_rotates_v(qkv, positions, qw, kw, *, num_q_heads, num_kv_heads, eps=1e-5, rope_base=1e4):
+    x = orig_qknr(qkv, positions, qw, kw, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads, eps=eps,
+                  rope_base=rope_base)
+    for g in range(num_kv_heads):
+        c = mod.v_cols(g, num_q_heads, num_kv_heads)
+        x[:, c] = orig_rope(orig_rms(x[:, c], kw, eps), positions, rope_base)
+    return x
+
+
+def _qknr_k_with_q_weight(qkv, positions, qw, kw, **kw2):
+    return orig_qknr(qkv, positions, qw, qw, **kw2)
+
+
+def _qknr_rope_then_norm(qkv, positions, qw, kw, *, num_q_heads, num_kv_heads, eps=1e-5, rope_base=1e4):
+    x = np.array(qkv, dtype=np.float64, copy=True)
+    pos = np.asarray(positions)
+    for h in range(num_q_heads):
+        c = mod.q_cols(h, num_q_heads, num_kv_heads)
+        x[:, c] = orig_rms(orig_rope(x[:, c], pos, rope_base), qw, eps)
+    for g in range(num_kv_heads):
+        c = mod.k_cols(g, num_q_heads, num_kv_heads)
+        x[:, c] = orig_rms(orig_rope(x[:, c], pos, rope_base), kw, eps)
+    return x
+
+
+def _qknr_skip_last_k(qkv, positions, qw, kw, *, num_q_heads, num_kv_heads, eps=1e-5, rope_base=1e4):
+    x = orig_qknr(qkv, positions, qw, kw, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads, eps=eps,
+                  rope_base=rope_base)
+    c = mod.k_cols(num_kv_heads - 1, num_q_heads, num_kv_heads)
+    x[:, c] = np.asarray(qkv, dtype=np.float64)[:, c]
+    return x
 
 
 def _rope_sign(x, pos, base):
@@ -101,6 +135,10 @@ MUTATIONS = {
     "softmax_wrong_axis": ("_softmax_attend", _attend_wrong_axis),
     "drop_block_keys": ("_softmax_attend", _attend_context_only),
     "values_are_keys": ("_softmax_attend", _attend_v_is_k),
+    "qknr_rotates_v": ("qk_norm_rope", _qknr_rotates_v),
+    "qknr_k_with_q_weight": ("qk_norm_rope", _qknr_k_with_q_weight),
+    "qknr_rope_then_norm": ("qk_norm_rope", _qknr_rope_then_norm),
+    "qknr_skip_last_k_head": ("qk_norm_rope", _qknr_skip_last_k),
 }
 
 
@@ -119,7 +157,8 @@ def _battery():
                 failed.append(f"bruteforce{i}")
         except Exception:  # any error is a failed pin
             failed.append(f"bruteforce{i}")
-    for name in ("test_rmsnorm_closed_forms", "test_rope_closed_forms"):
+    for name in ("test_rmsnorm_closed_forms", "test_rope_closed_forms", "test_qk_norm_rope_closed_forms",
+                 "test_qk_norm_rope_constant_heads_at_position_zero"):
         try:
             getattr(pins, name)()
         except Exception:  # any error is a failed pin

@@ -267,6 +267,103 @@ def test_rope_relative_position_property():
 
 
 # ---------------------------------------------------------------------------------------
+# fused_qk_norm_rope (the drafter's cell) on packed rows
+# ---------------------------------------------------------------------------------------
+
+_EXACT_FREQ = [(0, 1.0), (8, 0.1), (16, 0.01), (24, 0.001)]  # 10000**(-2i/64), exact decimals
+
+
+def test_qk_norm_rope_closed_forms():
+    # Hkv = 2 (12 q heads, 2 k heads, 2 v heads) + 16 padding columns.  Every q/k head of a
+    # row is a one-hot a*e_j: RMSNorm gives a*w_j/sqrt(a^2/64 + eps) at j, then the rotation
+    # puts cos/sin of p*f (exact angles) at (j, j+32) -- or (-sin, cos) for j >= 32.  q and k
+    # use different weight vectors; v heads and padding must come back unchanged.
+    Hq, Hkv, eps = 12, 2, 1e-5
+    wq = np.linspace(0.5, 1.5, 64)
+    wk = np.linspace(1.7, 0.3, 64)
+    rng = np.random.default_rng(21)
+    pos = np.array([0, 1, 7, 2041, 32775])
+    N = len(pos)
+    qkv = rng.standard_normal((N, (Hq + 2 * Hkv) * 64 + 16))
+    expect = qkv.copy()
+    heads = [(h, h * 64, wq) for h in range(Hq)] + [(Hq + g, (Hq + g) * 64, wk) for g in range(Hkv)]
+    for r in range(N):
+        for k, (h, c0, w) in enumerate(heads):
+            i, f = _EXACT_FREQ[(h + r) % 4]
+            j = i + 32 * ((h + 2 * r) % 2)          # the one-hot sits in the first or second half
+            a = (0.25 + 0.5 * k) * (-1.0) ** (h + r)
+            qkv[r, c0:c0 + 64] = 0.0
+            qkv[r, c0 + j] = a
+            n = a * w[j] / math.sqrt(a * a / 64 + eps)
+            expect[r, c0:c0 + 64] = 0.0
+            ang = pos[r] * f
+            if j < 32:
+                expect[r, c0 + j], expect[r, c0 + j + 32] = n * math.cos(ang), n * math.sin(ang)
+            else:
+                expect[r, c0 + j - 32], expect[r, c0 + j] = -n * math.sin(ang), n * math.cos(ang)
+    got = oracle.qk_norm_rope(qkv, pos, wq, wk, num_q_heads=Hq, num_kv_heads=Hkv, eps=eps)
+    np.testing.assert_allclose(got, expect, rtol=1e-12, atol=1e-12)
+    vcols = slice((Hq + Hkv) * 64, None)
+    np.testing.assert_array_equal(got[:, vcols], qkv[:, vcols])
+
+
+def test_qk_norm_rope_constant_heads_at_position_zero():
+    # position 0 rotates nothing: a constant head c becomes w * c / sqrt(c^2 + eps)
+    Hq, Hkv, eps = 6, 1, 1e-5
+    wq, wk = np.linspace(0.5, 1.5, 64), np.linspace(1.5, 0.5, 64)
+    qkv = np.zeros((3, 8 * 64))
+    cs = [0.3, -2.0, 5.0, 0.01, 1.0, -0.7, 3.3]
+    for r in range(3):
+        for h in range(Hq + Hkv):
+            qkv[r, h * 64:(h + 1) * 64] = cs[h] * (r + 1)
+    qkv[:, 7 * 64:] = np.arange(64)
+    got = oracle.qk_norm_rope(qkv, np.zeros(3, dtype=np.int64), wq, wk, num_q_heads=Hq, num_kv_heads=Hkv, eps=eps)
+    for r in range(3):
+        for h in range(Hq + Hkv):
+            c = cs[h] * (r + 1)
+            w = wq if h < Hq else wk
+            np.testing.assert_allclose(got[r, h * 64:(h + 1) * 64], w * c / math.sqrt(c * c + eps), rtol=1e-13)
+    np.testing.assert_array_equal(got[:, 7 * 64:], qkv[:, 7 * 64:])
+
+
+def test_qk_norm_rope_heads_and_rows_independent():
+    Hq, Hkv = 24, 4
+    rng = np.random.default_rng(5)
+    qkv = rng.standard_normal((6, 32 * 64))
+    pos = rng.integers(0, 40000, 6)
+    w1, w2 = rng.uniform(0.5, 1.5, 64), rng.uniform(0.5, 1.5, 64)
+    base = oracle.qk_norm_rope(qkv, pos, w1, w2, num_q_heads=Hq, num_kv_heads=Hkv)
+    for h in (0, 5, 23, 24, 27):
+        x = qkv.copy()
+        x[2, h * 64:(h + 1) * 64] *= -3.0
+        got = oracle.qk_norm_rope(x, pos, w1, w2, num_q_heads=Hq, num_kv_heads=Hkv)
+        changed = np.zeros_like(got, dtype=bool)
+        changed[2, h * 64:(h + 1) * 64] = True
+        np.testing.assert_array_equal(got[~changed], base[~changed])
+        # RMSNorm is odd and scale-free (up to eps): the head flips sign
+        np.testing.assert_allclose(got[2, h * 64:(h + 1) * 64], -base[2, h * 64:(h + 1) * 64], rtol=1e-5, atol=1e-9)
+
+
+def test_attention_of_norm_roped_rows_equals_qknorm_attention():
+    case = ds.make_config(2)
+    a = case.np_args()
+    ref = oracle.drafter_attn_qknorm(**a)
+    b = dict(a)
+    b["qkv"] = oracle.qk_norm_rope(a["qkv"], a["positions"], a["q_norm_weight"], a["k_norm_weight"],
+                                   num_q_heads=case.Hq, num_kv_heads=case.Hkv)
+    np.testing.assert_array_equal(oracle.drafter_attn(**b), ref)
+
+
+def test_qk_norm_rope_rejects_out_of_contract():
+    with pytest.raises(oracle.OracleContractError):
+        oracle.qk_norm_rope(np.zeros((2, 512)), np.zeros(3), np.ones(64), np.ones(64), num_q_heads=6, num_kv_heads=1)
+    with pytest.raises(oracle.OracleContractError):
+        oracle.qk_norm_rope(np.zeros((2, 500)), np.zeros(2), np.ones(64), np.ones(64), num_q_heads=6, num_kv_heads=1)
+    with pytest.raises(oracle.OracleContractError):
+        oracle.qk_norm_rope(np.zeros((2, 1024)), np.zeros(2), np.ones(64), np.ones(64), num_q_heads=12, num_kv_heads=1)
+
+
+# ---------------------------------------------------------------------------------------
 # invariants
 # ---------------------------------------------------------------------------------------
 
