@@ -283,6 +283,34 @@ def make_config(n: int, k: int = 0, poison: bool = False) -> DrafterCase:
     return CONFIGS[n](k, poison=poison)
 
 
+@dataclasses.dataclass
+class NormRopeRows:
+    """Inputs of the standalone q/k norm + rotation op: packed rows, one position each."""
+    qkv: torch.Tensor            # bf16 [N, (Hq + 2 Hkv) * 64 + pad]
+    positions: torch.Tensor      # int32 / int64 [N]
+    q_norm_weight: torch.Tensor  # bf16 [64]
+    k_norm_weight: torch.Tensor  # bf16 [64]
+    Hq: int
+    Hkv: int
+
+
+def make_norm_rope_rows(N: int, Hkv: int, *, seed: int, row_pad: int = 0, pos_dtype=torch.int32,
+                        pos_max: int = 40000, poison_pad: bool = False) -> NormRopeRows:
+    """Seeded rows: values ~ N(0,1), weights ~ U(0.5, 1.5), positions ~ U{0..pos_max};
+    padding columns are N(0,1) or, with poison_pad, NaN."""
+    rng = np.random.default_rng(seed)
+    Hq = 6 * Hkv
+    width = (Hq + 2 * Hkv) * 64
+    vals = rng.standard_normal((N, width + row_pad)).astype(np.float32)
+    if poison_pad and row_pad:
+        vals[:, width:] = np.nan
+    wq = rng.uniform(0.5, 1.5, 64)
+    wk = rng.uniform(0.5, 1.5, 64)
+    pos = rng.integers(0, pos_max + 1, N)
+    return NormRopeRows(qkv=_bf16(vals), positions=torch.from_numpy(pos).to(pos_dtype),
+                        q_norm_weight=_bf16(wq), k_norm_weight=_bf16(wk), Hq=Hq, Hkv=Hkv)
+
+
 def to_device(case: DrafterCase, device) -> DrafterCase:
     """Copy every tensor of a case to ``device`` (keeping the pool views' strides)."""
     d = dataclasses.replace(case)

@@ -44,8 +44,9 @@
  * that `stream` is a hipStream_t (NULL = the null stream).  The library
  * allocates nothing and never synchronises the host with the device: calls are
  * asynchronous in `stream` order and may be captured into a HIP graph.
- * Only `out`, `workspace` and `status_word` are written; qkv, the pools and the
- * page table are left bit-identical.
+ * The attention calls write only `out`, `workspace` and `status_word`; qkv, the
+ * pools and the page table are left bit-identical.  drafter_qk_norm_rope writes
+ * the q and k columns of qkv in place and nothing else.
  *
  * Errors: every shape, stride, alignment, aliasing and workspace check runs on
  * the host before any launch and returns a negative da_status with a message
@@ -90,6 +91,7 @@ enum {
 #define DA_HEAD_DIM 64
 #define DA_PAGE_SIZE 64
 #define DA_GQA 6
+#define DA_MAX_NORM_TOKENS 65536 /* rows per drafter_qk_norm_rope call */
 
 /*
  * Bytes of workspace a call with these sizes needs (0 for arguments outside the
@@ -162,6 +164,38 @@ int drafter_attn_qknorm(const void* qkv, int64_t qkv_row_stride,
                         void* out, int64_t out_row_stride,
                         int32_t* status_word,
                         void* stream);
+
+/*
+ * fused_qk_norm_rope, the drafter's cell (TensorRT-LLM PR #20532, Conversation,
+ * the commit adding fused_qk_norm_rope's drafter cell: head_dim 64, 6 query heads
+ * per KV head, 1 to 64 tokens, eps 1e-5, base 10000, NeoX; the attention commit
+ * says k3_drafter_attn_qknorm uses this op's arithmetic).  In place on qkv: in
+ * each of the num_tokens rows every query head is RMS-normalised with
+ * q_norm_weight and every key head with k_norm_weight (x * w / sqrt(mean(x^2) +
+ * eps), fp32), then NeoX-rotated (dims i and i + 32 by pos * base^(-2i/64), the
+ * angle reduced in fp64), and rounded to bf16 once.  Value heads and columns past
+ * the heads are not touched.  The arithmetic is the one drafter_attn_qknorm
+ * applies to the block's q and k, so drafter_attn on rows processed here gives
+ * bit-identical output to drafter_attn_qknorm on the original rows.
+ *
+ *   qkv        bf16 [num_tokens][qkv_row_stride] (device, read and written)
+ *   positions  int32 or int64 [num_tokens] (device)
+ *   q_norm_weight, k_norm_weight  bf16 [64] (device, 16-byte aligned)
+ *
+ * num_tokens in [1, DA_MAX_NORM_TOKENS]; num_q_heads = 6 * num_kv_heads,
+ * num_kv_heads in [1, 16]; head_dim 64 (else DA_EUNSUPPORTED); qkv 16-byte
+ * aligned, qkv_row_stride a multiple of 8 elements and >= (Hq + 2*Hkv) * 64;
+ * positions and the weights must not overlap qkv; eps finite >= 0, rope_base
+ * finite > 0.  Errors are returned before any launch (DA_EINVAL, DA_EUNSUPPORTED,
+ * DA_ELAUNCH) with a message in drafter_attn_last_error().  Asynchronous in
+ * `stream`; capturable.
+ */
+int drafter_qk_norm_rope(void* qkv, int64_t qkv_row_stride, int32_t num_tokens,
+                         int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                         const void* positions, int32_t positions_dtype,
+                         const void* q_norm_weight, const void* k_norm_weight,
+                         float eps, float rope_base,
+                         void* stream /* hipStream_t */);
 
 /* Message for the last non-DA_OK return on this thread ("" if none). */
 const char* drafter_attn_last_error(void);

@@ -11,5 +11,6 @@ from .ops import (  # noqa: F401
     drafter_attn_qknorm,
     make_workspace,
     plan,
+    qk_norm_rope,
     workspace_bytes,
 )

@@ -41,6 +41,14 @@ SIGNATURES = {
         c_vp, c_i64,
         c_vp, c_vp,
     ]),
+    "drafter_qk_norm_rope": (ctypes.c_int, [
+        c_vp, c_i64, c_i32,           # qkv, qkv_row_stride, num_tokens
+        c_i32, c_i32, c_i32,          # Hq, Hkv, head_dim
+        c_vp, c_i32,                  # positions, positions_dtype
+        c_vp, c_vp,                   # q_norm_weight, k_norm_weight
+        c_f32, c_f32,                 # eps, rope_base
+        c_vp,                         # stream
+    ]),
     "drafter_attn_last_error": (ctypes.c_char_p, []),
 }
 

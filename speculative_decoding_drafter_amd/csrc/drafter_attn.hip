@@ -412,6 +412,19 @@ __device__ __forceinline__ void flag(int32_t* status, int bit) {
   if (status) atomicOr(status, bit);
 }
 
+// (cos, sin) of the NeoX angle pos * base^(-2i/64) for frequency i < 32: the angle
+// is formed and reduced modulo 2 pi in fp64 (exact enough for any position an
+// int64 can carry into the reduction), then evaluated in fp32.
+__device__ __forceinline__ float2 rope_cos_sin(int64_t pos, int i, double log2_base) {
+  const double inv_freq = exp2(-static_cast<double>(i) * (1.0 / 32.0) * log2_base);  // base^(-2i/64)
+  const double th = static_cast<double>(pos) * inv_freq;
+  const double kq = rint(th * 0.15915494309189535);    // 1 / (2 pi)
+  const double red = fma(-kq, 6.283185307179586, th);  // |red| <= pi (+ tiny)
+  float sn, cn;
+  sincosf(static_cast<float>(red), &sn, &cn);
+  return make_float2(cn, sn);
+}
+
 // One 64-value head row held by 8 lanes (8 values each, lane u has dims 8u..8u+7):
 // RMSNorm with the weights' 8 bf16 values `wr` for those dims, then NeoX rotation
 // with the (cos, sin) row `cs`.
@@ -555,16 +568,7 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
   float2* cs = reinterpret_cast<float2*>(smem + kOffCS);
   // ---- a2/a3 (qknorm): rotation table, one (token, frequency) per thread
   if (QKNORM) {
-    if (tid < T * 32) {
-      const int i = tid & 31;
-      const double inv_freq = exp2(-static_cast<double>(i) * (1.0 / 32.0) * p.log2_base);  // base^(-2i/64)
-      const double th = static_cast<double>(pos) * inv_freq;
-      const double kq = rint(th * 0.15915494309189535);          // 1 / (2 pi)
-      const double red = fma(-kq, 6.283185307179586, th);        // |red| <= pi (+ tiny)
-      float sn, cn;
-      sincosf(static_cast<float>(red), &sn, &cn);
-      cs[tid] = make_float2(cn, sn);
-    }
+    if (tid < T * 32) cs[tid] = rope_cos_sin(pos, tid & 31, p.log2_base);
     __syncthreads();
   }
 
@@ -818,6 +822,60 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
 }
 
 // ---------------------------------------------------------------------------------
+// standalone q/k RMSNorm + NeoX RoPE, in place on the packed rows
+// ---------------------------------------------------------------------------------
+// Workgroup (x, y): tokens 8x .. 8x+7, and rows 32y .. 32y+31 of their list of
+// (token, q-or-k head) rows; 8 threads per row, 16 bytes each.  The row values,
+// norm weights and positions are loaded first; the rotation table of the 8 tokens
+// goes through LDS.  The arithmetic is the attention kernel's prologue
+// (rope_cos_sin, norm_rope_row), so these rows are bit-identical to the q/k rows
+// that kernel builds from the same inputs.
+constexpr int kNrTokens = 8;
+constexpr int kNrThreads = 256;
+constexpr int kNrRows = kNrThreads / 8;
+
+struct NrParams {
+  uint16_t* qkv;
+  int64_t qkv_stride;
+  const void* positions;
+  const uint16_t* wq;
+  const uint16_t* wk;
+  int32_t N, Hq, Hkv;
+  float eps;
+  double log2_base;
+};
+
+template <bool POS64>
+__global__ __launch_bounds__(kNrThreads) void qk_norm_rope_kernel(const NrParams p) {
+  __shared__ float2 cs[kNrTokens * 32];
+  const int tid = threadIdx.x, u = tid & 7;
+  const int t0 = blockIdx.x * kNrTokens;
+  const int nt = min(kNrTokens, p.N - t0);
+  const int heads = p.Hq + p.Hkv;
+  const int rr = blockIdx.y * kNrRows + (tid >> 3);  // row of this workgroup's (token, head) list
+  const int t = rr / heads, h = rr - t * heads;
+  const bool live = t < nt;
+  uint16_t* row = p.qkv + static_cast<int64_t>(t0 + t) * p.qkv_stride + h * kD + 8 * u;
+  u32x4 raw = {0u, 0u, 0u, 0u}, wraw = {0u, 0u, 0u, 0u};
+  if (live) {
+    raw = ld16(row);
+    wraw = ld16((h < p.Hq ? p.wq : p.wk) + 8 * u);
+  }
+  int64_t pos = 0;
+  if (tid < nt * 32)
+    pos = POS64 ? static_cast<const int64_t*>(p.positions)[t0 + (tid >> 5)]
+                : static_cast<int64_t>(static_cast<const int32_t*>(p.positions)[t0 + (tid >> 5)]);
+  if (tid < nt * 32) cs[tid] = rope_cos_sin(pos, tid & 31, p.log2_base);
+  __syncthreads();
+  if (live) {
+    float x[8];
+    unpack8(raw, x);
+    norm_rope_row(x, wraw, p.eps, cs + t * 32, u);
+    *reinterpret_cast<u32x4*>(row) = pack8(x);
+  }
+}
+
+// ---------------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------------
 
@@ -1002,6 +1060,15 @@ int launch_nt(const Params& p, const Plan& plan, hipStream_t stream) {
   return launch_t<3, QK, P64>(p, plan, stream);
 }
 
+template <bool P64>
+int launch_norm_rope(const NrParams& p, hipStream_t stream) {
+  dim3 grid((p.N + kNrTokens - 1) / kNrTokens, (kNrTokens * (p.Hq + p.Hkv) + kNrRows - 1) / kNrRows);
+  hipLaunchKernelGGL((qk_norm_rope_kernel<P64>), grid, dim3(kNrThreads), 0, stream, p);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(DA_ELAUNCH, std::string("launch failed: ") + hipGetErrorString(e));
+  return DA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1087,6 +1154,47 @@ int drafter_attn_qknorm(const void* qkv, int64_t qkv_row_stride, const void* k_p
   g_last_error.clear();
   hipStream_t st = static_cast<hipStream_t>(stream);
   return positions_dtype == DA_POS_INT64 ? launch_nt<true, true>(p, plan, st) : launch_nt<true, false>(p, plan, st);
+}
+
+int drafter_qk_norm_rope(void* qkv, int64_t qkv_row_stride, int32_t num_tokens, int32_t num_q_heads,
+                         int32_t num_kv_heads, int32_t head_dim, const void* positions, int32_t positions_dtype,
+                         const void* q_norm_weight, const void* k_norm_weight, float eps, float rope_base,
+                         void* stream) {
+  if (head_dim != kD) return fail(DA_EUNSUPPORTED, "head_dim must be 64");
+  if (num_kv_heads < 1 || num_kv_heads > DA_MAX_KV_HEADS) return fail(DA_EINVAL, "num_kv_heads must be in [1, 16]");
+  if (num_q_heads != kG * num_kv_heads) return fail(DA_EUNSUPPORTED, "num_q_heads must be 6 * num_kv_heads");
+  if (num_tokens < 1 || num_tokens > DA_MAX_NORM_TOKENS) return fail(DA_EINVAL, "num_tokens must be in [1, 65536]");
+  if (!qkv || !positions || !q_norm_weight || !k_norm_weight)
+    return fail(DA_EINVAL, "qkv, positions, q_norm_weight and k_norm_weight must be non-NULL");
+  const int64_t width = static_cast<int64_t>(num_q_heads + 2 * num_kv_heads) * kD;
+  if (qkv_row_stride < width) return fail(DA_EINVAL, "qkv_row_stride must be >= (Hq + 2*Hkv) * 64");
+  if (qkv_row_stride % 8) return fail(DA_EINVAL, "qkv_row_stride must be a multiple of 8 elements");
+  if (!aligned16(qkv) || !aligned16(q_norm_weight) || !aligned16(k_norm_weight))
+    return fail(DA_EINVAL, "qkv, q_norm_weight and k_norm_weight must be 16-byte aligned");
+  if (positions_dtype != DA_POS_INT32 && positions_dtype != DA_POS_INT64)
+    return fail(DA_EINVAL, "positions_dtype must be DA_POS_INT32 or DA_POS_INT64");
+  if (!(std::isfinite(eps) && eps >= 0.f)) return fail(DA_EINVAL, "eps must be finite and >= 0");
+  if (!(std::isfinite(rope_base) && rope_base > 0.f)) return fail(DA_EINVAL, "rope_base must be finite and > 0");
+  const size_t qkv_n = static_cast<size_t>(((num_tokens - 1) * qkv_row_stride + width) * 2);
+  const size_t pos_n = static_cast<size_t>(num_tokens) * (positions_dtype == DA_POS_INT64 ? 8 : 4);
+  if (overlaps(qkv, qkv_n, positions, pos_n) || overlaps(qkv, qkv_n, q_norm_weight, kD * 2) ||
+      overlaps(qkv, qkv_n, k_norm_weight, kD * 2))
+    return fail(DA_EINVAL, "qkv (written in place) overlaps positions or a norm weight");
+  NrParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.qkv = static_cast<uint16_t*>(qkv);
+  p.qkv_stride = qkv_row_stride;
+  p.positions = positions;
+  p.wq = static_cast<const uint16_t*>(q_norm_weight);
+  p.wk = static_cast<const uint16_t*>(k_norm_weight);
+  p.N = num_tokens;
+  p.Hq = num_q_heads;
+  p.Hkv = num_kv_heads;
+  p.eps = eps;
+  p.log2_base = std::log2(static_cast<double>(rope_base));
+  g_last_error.clear();
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return positions_dtype == DA_POS_INT64 ? launch_norm_rope<true>(p, st) : launch_norm_rope<false>(p, st);
 }
 
 const char* drafter_attn_last_error(void) { return g_last_error.c_str(); }

@@ -164,3 +164,30 @@ def drafter_attn_qknorm(qkv: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.T
         _ptr(status), _stream(a["dev"]))
     _raise(rc)
     return a["out"]
+
+
+def qk_norm_rope(qkv: torch.Tensor, positions: torch.Tensor, q_norm_weight: torch.Tensor,
+                 k_norm_weight: torch.Tensor, *, num_q_heads: int, num_kv_heads: int, eps: float = 1e-5,
+                 rope_base: float = 10000.0) -> torch.Tensor:
+    """fused_qk_norm_rope (the drafter's cell), in place on ``qkv`` [N, >= (Hq+2Hkv)*64] bf16.
+
+    Every q and k head of each row is RMS-normalised and NeoX-rotated at the row's
+    position; v heads and padding are left as they are.  Returns ``qkv``.
+    """
+    lib = _lib.load()
+    _check(qkv.device.type == "cuda", "qkv must be a GPU tensor (there is no CPU path)")
+    _check(qkv.dtype == torch.bfloat16 and qkv.dim() == 2 and qkv.stride(1) == 1,
+           "qkv must be bf16 [N, row_stride] with unit column stride")
+    N = int(qkv.shape[0])
+    Hq, Hkv = int(num_q_heads), int(num_kv_heads)
+    _check(qkv.shape[1] >= (Hq + 2 * Hkv) * HEAD_DIM, "qkv is narrower than (Hq + 2*Hkv) * 64")
+    _check(positions.dtype in POS_DTYPES and positions.dim() == 1 and positions.numel() == N
+           and positions.is_contiguous() and positions.device == qkv.device, "positions must be int32/int64 [N]")
+    for name, wt in (("q_norm_weight", q_norm_weight), ("k_norm_weight", k_norm_weight)):
+        _check(wt.dtype == torch.bfloat16 and tuple(wt.shape) == (HEAD_DIM,) and wt.is_contiguous()
+               and wt.device == qkv.device, f"{name} must be bf16 [64]")
+    rc = lib.drafter_qk_norm_rope(qkv.data_ptr(), qkv.stride(0), N, Hq, Hkv, HEAD_DIM, positions.data_ptr(),
+                                  POS_DTYPES[positions.dtype], q_norm_weight.data_ptr(), k_norm_weight.data_ptr(),
+                                  float(eps), float(rope_base), _stream(qkv.device))
+    _raise(rc)
+    return qkv

@@ -28,12 +28,12 @@ def lib():
 def _declared():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:size_t|int|const char\*)\s+(drafter_attn\w*)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:size_t|int|const char\*)\s+(drafter_\w*)\s*\(", text, flags=re.M)))
 
 
 def test_header_declares_entry_points():
     assert _declared() == sorted(["drafter_attn", "drafter_attn_qknorm", "drafter_attn_workspace_bytes",
-                                  "drafter_attn_plan", "drafter_attn_last_error"])
+                                  "drafter_attn_plan", "drafter_attn_last_error", "drafter_qk_norm_rope"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -164,3 +164,39 @@ def test_qknorm_specific_checks(lib):
     assert q(base=0.0) == DA_EINVAL
     assert q(positions=0xB00000) == DA_EINVAL   # out overlaps positions
     assert q(R=9) == DA_EINVAL
+
+
+def _nr(lib, **over):
+    """A drafter_qk_norm_rope call with fake (never dereferenced) pointers."""
+    a = dict(qkv=0x10000, stride=512, N=8, Hq=6, Hkv=1, hd=64, pos=0x900000, pdt=0, wq=0x900100, wk=0x900200,
+             eps=1e-5, base=10000.0)
+    a.update(over)
+    return lib.drafter_qk_norm_rope(a["qkv"], a["stride"], a["N"], a["Hq"], a["Hkv"], a["hd"], a["pos"], a["pdt"],
+                                    a["wq"], a["wk"], a["eps"], a["base"], None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(hd=128), DA_EUNSUPPORTED),
+    (dict(Hq=12), DA_EUNSUPPORTED),
+    (dict(Hkv=0, Hq=0), DA_EINVAL),
+    (dict(Hkv=17, Hq=102), DA_EINVAL),
+    (dict(N=0), DA_EINVAL),
+    (dict(N=65537), DA_EINVAL),
+    (dict(qkv=None), DA_EINVAL),
+    (dict(pos=None), DA_EINVAL),
+    (dict(wk=None), DA_EINVAL),
+    (dict(stride=500), DA_EINVAL),
+    (dict(stride=516), DA_EINVAL),
+    (dict(qkv=0x10008), DA_EINVAL),
+    (dict(wq=0x900108), DA_EINVAL),
+    (dict(pdt=2), DA_EINVAL),
+    (dict(eps=-1.0), DA_EINVAL),
+    (dict(eps=float("inf")), DA_EINVAL),
+    (dict(base=0.0), DA_EINVAL),
+    (dict(base=float("nan")), DA_EINVAL),
+    (dict(pos=0x10000 + 1024), DA_EINVAL),   # positions inside qkv (written in place)
+    (dict(wq=0x10000 + 4096), DA_EINVAL),
+])
+def test_norm_rope_invalid_arguments_rejected_before_launch(lib, over, code):
+    assert _nr(lib, **over) == code
+    assert _lib.last_error() != ""
