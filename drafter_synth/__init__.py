@@ -283,6 +283,34 @@ def make_config(n: int, k: int = 0, poison: bool = False) -> DrafterCase:
     return CONFIGS[n](k, poison=poison)
 
 
+def with_append_room(case: DrafterCase, seed: int) -> DrafterCase:
+    """The same case with room to append every block to its request's paged row.
+
+    Each request gets fresh pool pages for the logical pages its ``L + T``
+    tokens need beyond its context (pages added at the end of the pool, values
+    ~ N(0,1)), and the page table gets the columns to name them; no two
+    requests share a page.  Needs a case drawn with one pool tensor.
+    """
+    assert case.pool is not None, "needs a case with a single [P, 2, Hkv, 64, 64] pool"
+    rng = np.random.default_rng(seed)
+    lens = [int(x) for x in case.context_lens.tolist()]
+    have = [math.ceil(L / PAGE) for L in lens]
+    need = [math.ceil((L + case.T) / PAGE) for L in lens]
+    extra = sum(n - h for n, h in zip(need, have))
+    stride = max([case.stride] + need)
+    P = case.num_pages
+    add = _bf16(rng.standard_normal((extra, 2, case.Hkv, PAGE, HEAD_DIM), dtype=np.float32))
+    pool = torch.cat([case.pool, add], dim=0)
+    table = torch.from_numpy(rng.integers(0, P + extra, size=(case.R, stride))).to(torch.int32)
+    table[:, :case.stride] = case.page_table
+    nxt = P
+    for r in range(case.R):
+        for j in range(have[r], need[r]):
+            table[r, j] = nxt
+            nxt += 1
+    return dataclasses.replace(case, pool=pool, k_pool=pool[:, 0], v_pool=pool[:, 1], page_table=table)
+
+
 @dataclasses.dataclass
 class NormRopeRows:
     """Inputs of the standalone q/k norm + rotation op: packed rows, one position each."""

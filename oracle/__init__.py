@@ -14,5 +14,7 @@ from .drafter_attn_oracle import (  # noqa: F401
     drafter_attn_qknorm,
     drafter_attn_split_merge,
     qk_norm_rope,
+    kv_append,
+    paged_attn,
     OracleContractError,
 )

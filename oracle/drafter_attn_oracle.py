@@ -271,6 +271,72 @@ def qk_norm_rope(qkv, positions, q_norm_weight, k_norm_weight, *, num_q_heads: i
     return x
 
 
+# --------------------------------------------------------------------------------------
+# the path the fused kernel replaces (built as an A/B baseline): append, then attend
+# --------------------------------------------------------------------------------------
+
+def kv_append(k_pool, v_pool, qkv, page_table, context_lens, block_lens=None, *, num_q_heads: int,
+              num_kv_heads: int, tokens_per_block: int):
+    """append_paged_kv_cache as the replaced DFlash path uses it.
+
+    PR #20532, Conversation, the attention commit: the fused kernel reads the
+    block's K/V from qkv instead of appending them to the cache first and then
+    running a non-causal context kernel.  Token ``t < b_r`` of request ``r`` is
+    logical token ``L_r + t`` of the request, i.e. slot ``(L_r + t) % 64`` of
+    page ``page_table[r, (L_r + t) // 64]``; for every KV head ``g`` its K comes
+    from the block's k columns and its V from the v columns.  Returns new
+    ``(k_pool, v_pool)`` float64 copies; no other slot changes.
+    """
+    Hq, Hkv, T = int(num_q_heads), int(num_kv_heads), int(tokens_per_block)
+    k = np.array(k_pool, dtype=np.float64, copy=True)
+    v = np.array(v_pool, dtype=np.float64, copy=True)
+    qkv = np.asarray(qkv, dtype=np.float64)
+    R = len(context_lens)
+    stride = page_table.shape[1]
+    for r in range(R):
+        L = int(context_lens[r])
+        b = T if block_lens is None else int(block_lens[r])
+        if L < 0 or L + b > stride * PAGE:
+            raise OracleContractError(f"request {r}: {L} + {b} tokens do not fit {stride} pages")
+        for t in range(b):
+            phys = int(page_table[r, (L + t) // PAGE])
+            if not 0 <= phys < k.shape[0]:
+                raise OracleContractError(f"page id {phys} out of range")
+            slot = (L + t) % PAGE
+            for g in range(Hkv):
+                k[phys, g, slot] = qkv[r * T + t, k_cols(g, Hq, Hkv)]
+                v[phys, g, slot] = qkv[r * T + t, v_cols(g, Hq, Hkv)]
+    return k, v
+
+
+def paged_attn(qkv, k_pool, v_pool, page_table, kv_lens, block_lens=None, *, num_q_heads: int,
+               num_kv_heads: int, tokens_per_block: int, scale: Optional[float] = None) -> np.ndarray:
+    """The replaced path's non-causal context attention: the block's query rows of
+    request ``r`` attend to the first ``kv_lens[r]`` tokens of its paged row (the
+    context and, after ``kv_append``, the block itself); qkv supplies only the
+    queries.  Rows past the block length, and every row of a request with no
+    keys, are zero.
+    """
+    Hq, Hkv, T = int(num_q_heads), int(num_kv_heads), int(tokens_per_block)
+    if scale is None:
+        scale = 1.0 / math.sqrt(HEAD_DIM)
+    qkv = np.asarray(qkv, dtype=np.float64)
+    R = len(kv_lens)
+    out = np.zeros((R * T, Hq * HEAD_DIM), dtype=np.float64)
+    for r in range(R):
+        n = int(kv_lens[r])
+        b = T if block_lens is None else int(block_lens[r])
+        if n == 0:
+            continue
+        rows = slice(r * T, r * T + b)
+        kv = {g: gather_context(k_pool, v_pool, page_table[r], n, g) for g in range(Hkv)}
+        for h in range(Hq):
+            keys, vals = kv[kv_head_of(h)]
+            o, _ = _softmax_attend(qkv[rows, q_cols(h, Hq, Hkv)], keys, vals, scale)
+            out[rows, h * HEAD_DIM:(h + 1) * HEAD_DIM] = o
+    return out
+
+
 def drafter_attn_split_merge(qkv, k_pool, v_pool, page_table, context_lens, block_lens=None, *,
                              num_splits: int, num_q_heads: int, num_kv_heads: int,
                              tokens_per_block: int, scale: Optional[float] = None,

@@ -20,6 +20,22 @@ orig_freq = mod.rope_inv_freq
 orig_gather = mod.gather_context
 orig_attend = mod._softmax_attend
 orig_qknr = mod.qk_norm_rope
+orig_append = mod.kv_append
+orig_paged = mod.paged_attn
+
+
+def _append_next_slot(k_pool, v_pool, qkv, page_table, context_lens, block_lens=None, **kw):
+    return orig_append(k_pool, v_pool, qkv, page_table, np.asarray(context_lens) + 1, block_lens, **kw)
+
+
+def _append_v_as_k(k_pool, v_pool, qkv, page_table, context_lens, block_lens=None, **kw):
+    k, v = orig_append(k_pool, v_pool, qkv, page_table, context_lens, block_lens, **kw)
+    _, v2 = orig_append(v_pool, v_pool, qkv, page_table, context_lens, block_lens, **kw)
+    return np.where(k != np.asarray(k_pool), v2, k), v
+
+
+def _paged_drop_last(qkv, k_pool, v_pool, page_table, kv_lens, block_lens=None, **kw):
+    return orig_paged(qkv, k_pool, v_pool, page_table, np.maximum(np.asarray(kv_lens) - 1, 0), block_lens, **kw)
 
 
 def _qknr_rotates_v(qkv, positions, qw, kw, *, num_q_heads, num_kv_heads, eps=1e-5, rope_base=1e4):
@@ -139,6 +155,9 @@ MUTATIONS = {
     "qknr_k_with_q_weight": ("qk_norm_rope", _qknr_k_with_q_weight),
     "qknr_rope_then_norm": ("qk_norm_rope", _qknr_rope_then_norm),
     "qknr_skip_last_k_head": ("qk_norm_rope", _qknr_skip_last_k),
+    "append_next_slot": ("kv_append", _append_next_slot),
+    "append_v_as_k": ("kv_append", _append_v_as_k),
+    "paged_drops_last_key": ("paged_attn", _paged_drop_last),
 }
 
 
@@ -163,6 +182,11 @@ def _battery():
             getattr(pins, name)()
         except Exception:  # any error is a failed pin
             failed.append(name)
+    for i in (0, 1):
+        try:
+            pins.test_replaced_path_equals_fused_definition(i)
+        except Exception:  # any error is a failed pin
+            failed.append(f"replaced{i}")
     for where in ("first", "tail_slot", "block"):
         try:
             pins.test_needle(where)

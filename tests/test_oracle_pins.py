@@ -364,6 +364,82 @@ def test_qk_norm_rope_rejects_out_of_contract():
 
 
 # ---------------------------------------------------------------------------------------
+# the replaced path: append the block to the pool, then attend to the pool only
+# ---------------------------------------------------------------------------------------
+
+def _replaced(case: ds.DrafterCase):
+    """norm/rope (qknorm cases), kv_append, paged_attn over L + b keys -- all fp64."""
+    a = case.np_args()
+    kw = dict(num_q_heads=case.Hq, num_kv_heads=case.Hkv)
+    rows = a["qkv"]
+    if case.qknorm:
+        rows = oracle.qk_norm_rope(rows, a["positions"], a["q_norm_weight"], a["k_norm_weight"], **kw)
+    k, v = oracle.kv_append(a["k_pool"], a["v_pool"], rows, a["page_table"], a["context_lens"], a["block_lens"],
+                            tokens_per_block=case.T, **kw)
+    b = np.full(case.R, case.T) if a["block_lens"] is None else a["block_lens"]
+    return oracle.paged_attn(rows, k, v, a["page_table"], a["context_lens"] + b, a["block_lens"],
+                             tokens_per_block=case.T, scale=case.scale, **kw), (k, v)
+
+
+def _append_cases():
+    return [
+        ds.make_case(2, 3, 12, 2, [64, 130], seed=41, qknorm=True, pool_pages=6),
+        ds.make_case(3, 5, 6, 1, [0, 61, 127], seed=42, qknorm=False, pool_pages=5, stride=3),
+        ds.make_case(2, 8, 24, 4, [1, 2041], seed=43, qknorm=True, pool_pages=40, block_lens=[3, 8],
+                     pos_dtype=torch.int64),
+    ]
+
+
+@pytest.mark.parametrize("i", range(3))
+def test_replaced_path_equals_fused_definition(i):
+    # the fused op attends to the same keys in the same order as append + non-causal paged attention
+    case = ds.with_append_room(_append_cases()[i], seed=100 + i)
+    got, _ = _replaced(case)
+    np.testing.assert_array_equal(got, _oracle(case))
+
+
+def test_kv_append_writes_exactly_the_block_slots():
+    case = ds.with_append_room(ds.make_case(3, 5, 12, 2, [0, 61, 127], seed=44, pool_pages=5, stride=3,
+                                            block_lens=[5, 2, 4]), seed=7)
+    a = case.np_args()
+    k, v = oracle.kv_append(a["k_pool"], a["v_pool"], a["qkv"], a["page_table"], a["context_lens"],
+                            a["block_lens"], num_q_heads=12, num_kv_heads=2, tokens_per_block=5)
+    touched = np.zeros(k.shape[:3], dtype=bool)
+    for r, (L, b) in enumerate(zip([0, 61, 127], [5, 2, 4])):
+        for t in range(b):
+            page = a["page_table"][r, (L + t) // 64]
+            touched[page, :, (L + t) % 64] = True
+            for g in range(2):
+                np.testing.assert_array_equal(k[page, g, (L + t) % 64], a["qkv"][r * 5 + t, (12 + g) * 64:(13 + g) * 64])
+                np.testing.assert_array_equal(v[page, g, (L + t) % 64], a["qkv"][r * 5 + t, (14 + g) * 64:(15 + g) * 64])
+    np.testing.assert_array_equal(k[~touched], a["k_pool"][~touched])
+    np.testing.assert_array_equal(v[~touched], a["v_pool"][~touched])
+    assert touched.sum() == 2 * (5 + 2 + 4)
+
+
+def test_paged_attn_closed_forms():
+    case = ds.make_case(2, 4, 6, 1, [64, 5], seed=45, pool_pages=3)
+    a = case.np_args()
+    kw = dict(num_q_heads=6, num_kv_heads=1, tokens_per_block=4)
+    # no keys: zero rows; one key: every row returns that key's value
+    out0 = oracle.paged_attn(a["qkv"], a["k_pool"], a["v_pool"], a["page_table"], np.array([0, 0]), **kw)
+    np.testing.assert_array_equal(out0, 0.0)
+    out1 = oracle.paged_attn(a["qkv"], a["k_pool"], a["v_pool"], a["page_table"], np.array([1, 1]), **kw)
+    for r in range(2):
+        val = a["v_pool"][a["page_table"][r, 0], 0, 0]
+        for h in range(6):
+            np.testing.assert_allclose(out1[r * 4:(r + 1) * 4, h * 64:(h + 1) * 64], np.tile(val, (4, 1)), rtol=1e-15)
+
+
+def test_kv_append_rejects_overflow():
+    case = ds.make_case(1, 8, 6, 1, [60], seed=46, pool_pages=1)      # 60 + 8 > 64 slots
+    a = case.np_args()
+    with pytest.raises(oracle.OracleContractError):
+        oracle.kv_append(a["k_pool"], a["v_pool"], a["qkv"], a["page_table"], a["context_lens"], None,
+                         num_q_heads=6, num_kv_heads=1, tokens_per_block=8)
+
+
+# ---------------------------------------------------------------------------------------
 # invariants
 # ---------------------------------------------------------------------------------------
 
