@@ -46,7 +46,8 @@
  * asynchronous in `stream` order and may be captured into a HIP graph.
  * The attention calls write only `out`, `workspace` and `status_word`; qkv, the
  * pools and the page table are left bit-identical.  drafter_qk_norm_rope writes
- * the q and k columns of qkv in place and nothing else.
+ * the q and k columns of qkv in place and nothing else; drafter_kv_append writes
+ * the block's slots of the pools (and status_word) and nothing else.
  *
  * Errors: every shape, stride, alignment, aliasing and workspace check runs on
  * the host before any launch and returns a negative da_status with a message
@@ -196,6 +197,60 @@ int drafter_qk_norm_rope(void* qkv, int64_t qkv_row_stride, int32_t num_tokens,
                          const void* q_norm_weight, const void* k_norm_weight,
                          float eps, float rope_base,
                          void* stream /* hipStream_t */);
+
+/*
+ * The path the fused op replaces, built here as an A/B baseline (TensorRT-LLM PR
+ * #20532, Conversation, the attention commit: the fused kernel reads the block's
+ * K/V from qkv instead of appending them to the cache with append_paged_kv_cache
+ * and then running a non-causal context kernel).  Run as drafter_qk_norm_rope (in
+ * the qknorm case), drafter_kv_append, then drafter_paged_attn with kv_lens = L + b,
+ * it computes the same attention as drafter_attn(_qknorm) on the original rows, at
+ * the cost of three launches and pool writes.
+ *
+ * drafter_kv_append: for every request r, token t < b_r (block_lens, NULL = all T)
+ * and KV head g, copies the block's K row (qkv columns (Hq + g) * 64 ..) and V row
+ * (columns (Hq + Hkv + g) * 64 ..) to slot (L_r + t) % 64 of page
+ * page_table[r * page_table_stride + (L_r + t) / 64] of k_pool / v_pool (device,
+ * written).  Layouts, alignment and size limits as for drafter_attn;
+ * page_table_stride >= 1.  The pools must not overlap qkv, the page table, the
+ * lengths or status_word.  On the device, a request whose L_r + b_r exceeds
+ * page_table_stride * 64 is skipped (DA_FLAG_CONTEXT_LEN), a token whose page id
+ * is out of [0, num_pages) is skipped (DA_FLAG_PAGE_ID), a b_r outside [1, T] is
+ * clamped (DA_FLAG_BLOCK_LEN).  Distinct requests must name distinct pages for
+ * their appended slots (two writers of one slot race).
+ */
+int drafter_kv_append(const void* qkv, int64_t qkv_row_stride,
+                      void* k_pool, void* v_pool, int64_t pool_page_stride,
+                      int32_t num_pages,
+                      const int32_t* page_table, int32_t page_table_stride,
+                      const int32_t* context_lens, const int32_t* block_lens /* NULL = all T */,
+                      int32_t num_requests, int32_t tokens_per_block,
+                      int32_t num_q_heads, int32_t num_kv_heads,
+                      int32_t head_dim, int32_t page_size,
+                      int32_t* status_word /* NULL = off */,
+                      void* stream /* hipStream_t */);
+
+/*
+ * drafter_paged_attn: non-causal paged attention of the block's query rows (q
+ * columns of qkv; its k/v columns are not read) over the first kv_lens[r] tokens
+ * of each request's paged row only -- no own-block keys are added.  Arguments,
+ * layouts, workspace, errors and flags as for drafter_attn, with kv_lens in place
+ * of context_lens (kv_lens[r] <= page_table_stride * 64).  A request with no key
+ * gets zero rows; rows past the block length are zero.
+ */
+int drafter_paged_attn(const void* qkv, int64_t qkv_row_stride,
+                       const void* k_pool, const void* v_pool, int64_t pool_page_stride,
+                       int32_t num_pages,
+                       const int32_t* page_table, int32_t page_table_stride,
+                       const int32_t* kv_lens, const int32_t* block_lens /* NULL = all T */,
+                       int32_t num_requests, int32_t tokens_per_block,
+                       int32_t num_q_heads, int32_t num_kv_heads,
+                       int32_t head_dim, int32_t page_size,
+                       float scale,
+                       void* workspace, size_t workspace_bytes,
+                       void* out, int64_t out_row_stride,
+                       int32_t* status_word /* NULL = off */,
+                       void* stream /* hipStream_t */);
 
 /* Message for the last non-DA_OK return on this thread ("" if none). */
 const char* drafter_attn_last_error(void);

@@ -9,7 +9,9 @@ from .ops import (  # noqa: F401
     DrafterAttnError,
     drafter_attn,
     drafter_attn_qknorm,
+    kv_append,
     make_workspace,
+    paged_attn,
     plan,
     qk_norm_rope,
     workspace_bytes,

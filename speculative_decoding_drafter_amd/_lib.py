@@ -49,6 +49,27 @@ SIGNATURES = {
         c_f32, c_f32,                 # eps, rope_base
         c_vp,                         # stream
     ]),
+    "drafter_kv_append": (ctypes.c_int, [
+        c_vp, c_i64,                  # qkv, qkv_row_stride
+        c_vp, c_vp, c_i64, c_i32,     # k_pool, v_pool, pool_page_stride, num_pages
+        c_vp, c_i32,                  # page_table, page_table_stride
+        c_vp, c_vp,                   # context_lens, block_lens
+        c_i32, c_i32, c_i32, c_i32,   # R, T, Hq, Hkv
+        c_i32, c_i32,                 # head_dim, page_size
+        c_vp, c_vp,                   # status_word, stream
+    ]),
+    "drafter_paged_attn": (ctypes.c_int, [
+        c_vp, c_i64,
+        c_vp, c_vp, c_i64, c_i32,
+        c_vp, c_i32,
+        c_vp, c_vp,                   # kv_lens, block_lens
+        c_i32, c_i32, c_i32, c_i32,
+        c_i32, c_i32,
+        c_f32,
+        c_vp, c_sz,
+        c_vp, c_i64,
+        c_vp, c_vp,
+    ]),
     "drafter_attn_last_error": (ctypes.c_char_p, []),
 }
 

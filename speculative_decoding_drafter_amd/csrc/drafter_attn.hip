@@ -476,7 +476,10 @@ __device__ __forceinline__ u32x4 pack8(const float (&x)[8]) {
 // ---------------------------------------------------------------------------------
 // the kernel
 // ---------------------------------------------------------------------------------
-template <int NT, bool QKNORM, bool POS64>
+// OWN = false is the attention of the path the fused op replaces: the block's
+// queries attend to pooled keys only (the caller appended the block to the pool and
+// passes kv lengths L + b), nothing is read from qkv but the queries.
+template <int NT, bool QKNORM, bool POS64, bool OWN = true>
 __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kSmemBytes];
   const int s = blockIdx.x, g = blockIdx.y, r = blockIdx.z;
@@ -502,7 +505,7 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
   const int cand = first < row_end ? (row_end - first + kWaves - 1) / kWaves : 0;
   int id = 0;
   if (lane < cand) id = p.page_table[static_cast<int64_t>(r) * p.pt_stride + first + kWaves * lane];
-  const bool own = (s == p.S - 1);
+  const bool own = OWN && s == p.S - 1;
   // Thread (sub, u) holds dims 8u .. 8u+7 of one head row: query row sub = 6t + h
   // of the tile (sub < 6T), or, in the last split, row j < T of the block's own K
   // (sub = 48 + j) or V (sub = 56 + j).  Rows past the block length are loaded
@@ -730,10 +733,10 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
   uint16_t* out_row = p.out + static_cast<int64_t>(r * T + t_row) * p.out_stride + (kG * g + row - kG * t_row) * kD +
                       4 * oc;
   if (p.S == 1) {
-    // a single split: its merged state is the answer (the block's own keys are
-    // in it, so l_wg > 0)
+    // a single split: its merged state is the answer (l_wg > 0 unless there is no
+    // key at all, possible only without the block's own keys: zero rows then)
     if (row_thread) {
-      const float inv = 1.0f / l_wg;
+      const float inv = l_wg > 0.f ? 1.0f / l_wg : 0.f;
       float x[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) x[j] = (t_row < b) ? acc[j] * inv : 0.f;
@@ -813,8 +816,8 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
       }
     }
   }
-  // den > 0: the last split holds the block's own keys
-  const float inv = 1.0f / den;
+  // den > 0 whenever there is a key (always with the block's own keys)
+  const float inv = den > 0.f ? 1.0f / den : 0.f;
   float x[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) x[j] = (t_row < b) ? acc[j] * inv : 0.f;
@@ -873,6 +876,43 @@ __global__ __launch_bounds__(kNrThreads) void qk_norm_rope_kernel(const NrParams
     norm_rope_row(x, wraw, p.eps, cs + t * 32, u);
     *reinterpret_cast<u32x4*>(row) = pack8(x);
   }
+}
+
+// ---------------------------------------------------------------------------------
+// append the block's K/V to the pool (the path the fused op replaces)
+// ---------------------------------------------------------------------------------
+// Workgroup (r, g): 8 tokens x (K, V) x 8 lanes of 16 bytes.  Token t < b of
+// request r goes to logical slot L + t of its paged row.  A request whose L + b
+// does not fit its row, and a token whose page id is out of range, is skipped and
+// flagged (writing elsewhere would corrupt the pool).
+constexpr int kApThreads = kMaxT * 2 * 8;
+
+__global__ __launch_bounds__(kApThreads) void kv_append_kernel(const Params p) {
+  const int r = blockIdx.x, g = blockIdx.y;
+  const int tid = threadIdx.x, t = tid >> 4, is_v = (tid >> 3) & 1, u = tid & 7;
+  const int T = p.T;
+  const int L = p.ctx_lens[r];
+  int b = p.blk_lens ? p.blk_lens[r] : T;
+  if (b < 1 || b > T) {
+    if (tid == 0 && g == 0) flag(p.status, DA_FLAG_BLOCK_LEN);
+    b = b < 1 ? 1 : T;
+  }
+  if (L < 0 || L + b > p.pt_stride * kPage) {
+    if (tid == 0 && g == 0) flag(p.status, DA_FLAG_CONTEXT_LEN);
+    return;
+  }
+  if (t >= b) return;
+  const int logical = L + t;
+  const int id = p.page_table[static_cast<int64_t>(r) * p.pt_stride + logical / kPage];
+  if (id < 0 || id >= p.num_pages) {
+    flag(p.status, DA_FLAG_PAGE_ID);
+    return;
+  }
+  const int col = (is_v ? p.Hq + p.Hkv + g : p.Hq + g) * kD + 8 * u;
+  const u32x4 val = ld16(p.qkv + static_cast<int64_t>(r * T + t) * p.qkv_stride + col);
+  uint16_t* pool = const_cast<uint16_t*>(is_v ? p.vpool : p.kpool);
+  *reinterpret_cast<u32x4*>(pool + static_cast<int64_t>(id) * p.page_stride +
+                            (static_cast<int64_t>(g) * kPage + logical % kPage) * kD + 8 * u) = val;
 }
 
 // ---------------------------------------------------------------------------------
@@ -1043,21 +1083,21 @@ Params make_params(const Common& a, const Plan& plan) {
   return p;
 }
 
-template <int NT, bool QK, bool P64>
+template <int NT, bool QK, bool P64, bool OWN>
 int launch_t(const Params& p, const Plan& plan, hipStream_t stream) {
   dim3 grid(plan.S, p.Hkv, p.R);
-  hipLaunchKernelGGL((drafter_attn_kernel<NT, QK, P64>), grid, dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((drafter_attn_kernel<NT, QK, P64, OWN>), grid, dim3(kThreads), 0, stream, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(DA_ELAUNCH, std::string("launch failed: ") + hipGetErrorString(e));
   return DA_OK;
 }
 
-template <bool QK, bool P64>
+template <bool QK, bool P64, bool OWN = true>
 int launch_nt(const Params& p, const Plan& plan, hipStream_t stream) {
   const int nt = (kG * p.T + 15) / 16;
-  if (nt == 1) return launch_t<1, QK, P64>(p, plan, stream);
-  if (nt == 2) return launch_t<2, QK, P64>(p, plan, stream);
-  return launch_t<3, QK, P64>(p, plan, stream);
+  if (nt == 1) return launch_t<1, QK, P64, OWN>(p, plan, stream);
+  if (nt == 2) return launch_t<2, QK, P64, OWN>(p, plan, stream);
+  return launch_t<3, QK, P64, OWN>(p, plan, stream);
 }
 
 template <bool P64>
@@ -1195,6 +1235,84 @@ int drafter_qk_norm_rope(void* qkv, int64_t qkv_row_stride, int32_t num_tokens, 
   g_last_error.clear();
   hipStream_t st = static_cast<hipStream_t>(stream);
   return positions_dtype == DA_POS_INT64 ? launch_norm_rope<true>(p, st) : launch_norm_rope<false>(p, st);
+}
+
+int drafter_paged_attn(const void* qkv, int64_t qkv_row_stride, const void* k_pool, const void* v_pool,
+                       int64_t pool_page_stride, int32_t num_pages, const int32_t* page_table,
+                       int32_t page_table_stride, const int32_t* kv_lens, const int32_t* block_lens,
+                       int32_t num_requests, int32_t tokens_per_block, int32_t num_q_heads, int32_t num_kv_heads,
+                       int32_t head_dim, int32_t page_size, float scale, void* workspace, size_t workspace_bytes,
+                       void* out, int64_t out_row_stride, int32_t* status_word, void* stream) {
+  const Common a{qkv, qkv_row_stride, k_pool, v_pool, pool_page_stride, num_pages, page_table, page_table_stride,
+                 kv_lens, block_lens, num_requests, tokens_per_block, num_q_heads, num_kv_heads, head_dim,
+                 page_size, scale, workspace, workspace_bytes, out, out_row_stride, status_word, stream};
+  const size_t need = drafter_attn_workspace_bytes(num_requests, tokens_per_block, num_q_heads, num_kv_heads,
+                                                   page_table_stride);
+  int rc = validate(a, need);
+  if (rc != DA_OK) return rc;
+  const Plan plan = make_plan(num_requests, num_kv_heads, page_table_stride);
+  Params p = make_params(a, plan);
+  g_last_error.clear();
+  return launch_nt<false, false, false>(p, plan, static_cast<hipStream_t>(stream));
+}
+
+int drafter_kv_append(const void* qkv, int64_t qkv_row_stride, void* k_pool, void* v_pool, int64_t pool_page_stride,
+                      int32_t num_pages, const int32_t* page_table, int32_t page_table_stride,
+                      const int32_t* context_lens, const int32_t* block_lens, int32_t num_requests,
+                      int32_t tokens_per_block, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t page_size, int32_t* status_word, void* stream) {
+  int rc = check_sizes(num_requests, tokens_per_block, num_q_heads, num_kv_heads, head_dim, page_size,
+                       page_table_stride);
+  if (rc != DA_OK) return rc;
+  if (!qkv || !k_pool || !v_pool || !page_table || !context_lens)
+    return fail(DA_EINVAL, "qkv, k_pool, v_pool, page_table and context_lens must be non-NULL");
+  if (page_table_stride < 1) return fail(DA_EINVAL, "page_table_stride must be >= 1 (the block needs a page)");
+  if (num_pages < 1) return fail(DA_EINVAL, "num_pages must be >= 1");
+  if (pool_page_stride < static_cast<int64_t>(num_kv_heads) * kPage * kD)
+    return fail(DA_EINVAL, "pool_page_stride must be >= num_kv_heads * 64 * 64");
+  if (pool_page_stride % 8) return fail(DA_EINVAL, "pool_page_stride must be a multiple of 8 elements");
+  if (!aligned16(k_pool) || !aligned16(v_pool) || !aligned16(qkv))
+    return fail(DA_EINVAL, "qkv, k_pool and v_pool must be 16-byte aligned");
+  const int64_t width = static_cast<int64_t>(num_q_heads + 2 * num_kv_heads) * kD;
+  if (qkv_row_stride < width) return fail(DA_EINVAL, "qkv_row_stride must be >= (Hq + 2*Hkv) * 64");
+  if (qkv_row_stride % 8) return fail(DA_EINVAL, "qkv_row_stride must be a multiple of 8 elements");
+  // the pools are written: they must not overlap anything the kernel reads or writes besides themselves
+  const int64_t rows = static_cast<int64_t>(num_requests) * tokens_per_block;
+  const size_t pool_n = static_cast<size_t>(((static_cast<int64_t>(num_pages) - 1) * pool_page_stride +
+                                             static_cast<int64_t>(num_kv_heads) * kPage * kD) * 2);
+  const size_t qkv_n = static_cast<size_t>(((rows - 1) * qkv_row_stride + width) * 2);
+  const size_t pt_n = static_cast<size_t>(num_requests) * page_table_stride * 4;
+  const size_t r_n = static_cast<size_t>(num_requests) * 4;
+  const struct { const void* p; size_t n; const char* name; } ins[] = {
+      {qkv, qkv_n, "qkv"}, {page_table, pt_n, "page_table"}, {context_lens, r_n, "context_lens"},
+      {block_lens, r_n, "block_lens"}, {status_word, 4, "status_word"}};
+  for (const auto& in : ins) {
+    if (overlaps(k_pool, pool_n, in.p, in.n) || overlaps(v_pool, pool_n, in.p, in.n))
+      return fail(DA_EINVAL, std::string("the pool overlaps ") + in.name);
+  }
+  Params p;
+  std::memset(&p, 0, sizeof(p));
+  p.qkv = static_cast<const uint16_t*>(qkv);
+  p.qkv_stride = qkv_row_stride;
+  p.kpool = static_cast<const uint16_t*>(k_pool);
+  p.vpool = static_cast<const uint16_t*>(v_pool);
+  p.page_stride = pool_page_stride;
+  p.page_table = page_table;
+  p.ctx_lens = context_lens;
+  p.blk_lens = block_lens;
+  p.status = status_word;
+  p.num_pages = num_pages;
+  p.pt_stride = page_table_stride;
+  p.R = num_requests;
+  p.T = tokens_per_block;
+  p.Hq = num_q_heads;
+  p.Hkv = num_kv_heads;
+  g_last_error.clear();
+  hipLaunchKernelGGL(kv_append_kernel, dim3(num_requests, num_kv_heads), dim3(kApThreads), 0,
+                     static_cast<hipStream_t>(stream), p);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(DA_ELAUNCH, std::string("launch failed: ") + hipGetErrorString(e));
+  return DA_OK;
 }
 
 const char* drafter_attn_last_error(void) { return g_last_error.c_str(); }

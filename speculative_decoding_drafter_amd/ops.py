@@ -191,3 +191,52 @@ def qk_norm_rope(qkv: torch.Tensor, positions: torch.Tensor, q_norm_weight: torc
                                   float(eps), float(rope_base), _stream(qkv.device))
     _raise(rc)
     return qkv
+
+
+def kv_append(qkv: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, page_table: torch.Tensor,
+              context_lens: torch.Tensor, *, num_q_heads: int, num_kv_heads: int, tokens_per_block: int,
+              block_lens: Optional[torch.Tensor] = None, status: Optional[torch.Tensor] = None) -> None:
+    """append_paged_kv_cache of the replaced path: the block's K/V rows go to slots L..L+b-1 of
+    each request's paged row (in place on the pools)."""
+    lib = _lib.load()
+    dev = qkv.device
+    _check(dev.type == "cuda", "qkv must be a GPU tensor (there is no CPU path)")
+    R, T = int(context_lens.shape[0]), int(tokens_per_block)
+    _check(page_table.dtype == torch.int32 and page_table.dim() == 2 and page_table.shape[0] == R
+           and page_table.is_contiguous(), "page_table must be contiguous int32 [R, stride]")
+    _check(context_lens.dtype == torch.int32 and context_lens.is_contiguous(), "context_lens must be int32 [R]")
+    _check(qkv.dtype == torch.bfloat16 and qkv.dim() == 2 and qkv.stride(1) == 1 and qkv.shape[0] == R * T,
+           "qkv must be bf16 [R*T, row_stride]")
+    for name, pool in (("k_pool", k_pool), ("v_pool", v_pool)):
+        _check(pool.dtype == torch.bfloat16 and pool.dim() == 4 and tuple(pool.shape[1:]) == (num_kv_heads, PAGE, HEAD_DIM)
+               and pool.stride()[1:] == (PAGE * HEAD_DIM, HEAD_DIM, 1) and pool.device == dev,
+               f"{name} must be bf16 [P, Hkv, 64, 64] with contiguous pages on {dev}")
+    if block_lens is not None:
+        _check(block_lens.dtype == torch.int32 and tuple(block_lens.shape) == (R,) and block_lens.is_contiguous(),
+               "block_lens must be int32 [R]")
+    rc = lib.drafter_kv_append(qkv.data_ptr(), qkv.stride(0), k_pool.data_ptr(), v_pool.data_ptr(), k_pool.stride(0),
+                               k_pool.shape[0], page_table.data_ptr(), page_table.shape[1], context_lens.data_ptr(),
+                               _ptr(block_lens), R, T, int(num_q_heads), int(num_kv_heads), HEAD_DIM, PAGE,
+                               _ptr(status), _stream(dev))
+    _raise(rc)
+
+
+def paged_attn(qkv: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, page_table: torch.Tensor,
+               kv_lens: torch.Tensor, *, num_q_heads: int, num_kv_heads: int, tokens_per_block: int,
+               block_lens: Optional[torch.Tensor] = None, scale: Optional[float] = None,
+               out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+               status: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The replaced path's non-causal context attention: the block's queries over the first
+    kv_lens[r] pooled tokens only.  Returns ``out`` [R*T, Hq*64] bf16."""
+    lib = _lib.load()
+    a = _common(qkv, k_pool, v_pool, page_table, kv_lens, block_lens, num_q_heads, num_kv_heads,
+                tokens_per_block, out, workspace)
+    scale = 1.0 / math.sqrt(HEAD_DIM) if scale is None else float(scale)
+    rc = lib.drafter_paged_attn(
+        qkv.data_ptr(), qkv.stride(0), k_pool.data_ptr(), v_pool.data_ptr(), k_pool.stride(0), k_pool.shape[0],
+        _ptr(page_table) if a["stride"] else None, a["stride"], kv_lens.data_ptr(), _ptr(block_lens),
+        a["R"], a["T"], a["Hq"], a["Hkv"], HEAD_DIM, PAGE, scale,
+        a["workspace"].data_ptr(), a["workspace"].numel(), a["out"].data_ptr(), a["out"].stride(0),
+        _ptr(status), _stream(a["dev"]))
+    _raise(rc)
+    return a["out"]

@@ -33,7 +33,8 @@ def _declared():
 
 def test_header_declares_entry_points():
     assert _declared() == sorted(["drafter_attn", "drafter_attn_qknorm", "drafter_attn_workspace_bytes",
-                                  "drafter_attn_plan", "drafter_attn_last_error", "drafter_qk_norm_rope"])
+                                  "drafter_attn_plan", "drafter_attn_last_error", "drafter_qk_norm_rope",
+                                  "drafter_kv_append", "drafter_paged_attn"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -200,3 +201,50 @@ def _nr(lib, **over):
 def test_norm_rope_invalid_arguments_rejected_before_launch(lib, over, code):
     assert _nr(lib, **over) == code
     assert _lib.last_error() != ""
+
+
+def _ap(lib, **over):
+    """A drafter_kv_append call with fake (never dereferenced) pointers."""
+    a = dict(qkv=0x10000, qs=512, kp=0x200000, vp=0x200000 + 8192, ps=16384, np_=4, pt=0x900000, pts=2,
+             cl=0x900100, bl=None, R=1, T=8, Hq=6, Hkv=1, hd=64, pg=64, st=None)
+    a.update(over)
+    return lib.drafter_kv_append(a["qkv"], a["qs"], a["kp"], a["vp"], a["ps"], a["np_"], a["pt"], a["pts"], a["cl"],
+                                 a["bl"], a["R"], a["T"], a["Hq"], a["Hkv"], a["hd"], a["pg"], a["st"], None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(hd=128), DA_EUNSUPPORTED),
+    (dict(Hq=12), DA_EUNSUPPORTED),
+    (dict(R=9), DA_EINVAL),
+    (dict(T=0), DA_EINVAL),
+    (dict(pts=0), DA_EINVAL),
+    (dict(pt=None), DA_EINVAL),
+    (dict(kp=None), DA_EINVAL),
+    (dict(cl=None), DA_EINVAL),
+    (dict(np_=0), DA_EINVAL),
+    (dict(ps=4095), DA_EINVAL),
+    (dict(qs=500), DA_EINVAL),
+    (dict(kp=0x200008), DA_EINVAL),
+    (dict(qkv=0x200000 + 100 * 1024), DA_EINVAL),   # qkv inside the pool (written)
+    (dict(pt=0x200000 + 1024), DA_EINVAL),          # page table inside the pool
+    (dict(st=0x200000 + 64), DA_EINVAL),            # status word inside the pool
+])
+def test_kv_append_invalid_arguments_rejected_before_launch(lib, over, code):
+    assert _ap(lib, **over) == code
+    assert _lib.last_error() != ""
+
+
+def test_paged_attn_shares_the_attention_checks(lib):
+    # same argument list and host checks as drafter_attn (kv_lens in place of context_lens)
+    def call(**o):
+        a = dict(qkv=0x10000, out=0xB00000, ws=0xA00000, wsb=1 << 20, hd=64, T=8)
+        a.update(o)
+        return lib.drafter_paged_attn(a["qkv"], 512, 0x200000, 0x202000, 16384, 4, 0x900000, 1, 0x900100, None,
+                                      1, a["T"], 6, 1, a["hd"], 64, 0.125, a["ws"], a["wsb"], a["out"], 384,
+                                      None, None)
+    assert call(hd=128) == DA_EUNSUPPORTED
+    assert call(T=9) == DA_EINVAL
+    assert call(ws=None) == DA_EWORKSPACE
+    assert call(ws=0xA00010) == DA_EWORKSPACE
+    assert call(out=0x10000 + 256) == DA_EINVAL
+    assert call(qkv=0x10008) == DA_EINVAL

@@ -1,0 +1,133 @@
+"""The path the fused op replaces, built as an A/B baseline, on the GPU.
+
+drafter_kv_append (bit-exact against the oracle's append: it copies bf16 rows),
+drafter_paged_attn (against the oracle, the acceptance bar), and the whole
+replaced path -- norm/rope, append, paged attention over L + b keys -- against
+the fp64 definition of the fused op and against the fused kernel itself.
+"""
+import numpy as np
+import pytest
+import torch
+
+import drafter_synth as ds
+import oracle
+from tests.gpu_util import check, reference, say, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _cases():
+    return {
+        "mixed": ds.make_case(3, 5, 12, 2, [0, 61, 127], seed=61, pool_pages=5, stride=3, block_lens=[5, 2, 4]),
+        "qknorm": ds.make_case(2, 8, 24, 4, [1, 2041], seed=62, qknorm=True, pool_pages=40, block_lens=[3, 8],
+                               pos_dtype=torch.int64),
+        "cfg2": ds.make_config(2),
+        "cfg3": ds.make_config(3),
+    }
+
+
+def _append_gpu(case, g, status=None):
+    from speculative_decoding_drafter_amd import kv_append
+
+    kv_append(g.qkv, g.k_pool, g.v_pool, g.page_table, g.context_lens, num_q_heads=case.Hq,
+              num_kv_heads=case.Hkv, tokens_per_block=case.T, block_lens=g.block_lens, status=status)
+
+
+@pytest.mark.parametrize("name", ["mixed", "qknorm", "cfg2", "cfg3"])
+def test_kv_append_bit_exact(name):
+    case = ds.with_append_room(_cases()[name], seed=70)
+    g = ds.to_device(case, "cuda")
+    say(f"append {name}")
+    _append_gpu(case, g)
+    a = case.np_args()
+    k, v = oracle.kv_append(a["k_pool"], a["v_pool"], a["qkv"], a["page_table"], a["context_lens"], a["block_lens"],
+                            num_q_heads=case.Hq, num_kv_heads=case.Hkv, tokens_per_block=case.T)
+    assert np.array_equal(g.k_pool.double().cpu().numpy(), k)
+    assert np.array_equal(g.v_pool.double().cpu().numpy(), v)
+
+
+@pytest.mark.parametrize("name", ["mixed", "qknorm", "cfg2", "cfg3"])
+def test_replaced_path_matches_fused_definition(name):
+    from speculative_decoding_drafter_amd import drafter_attn, drafter_attn_qknorm, paged_attn, qk_norm_rope
+
+    case = ds.with_append_room(_cases()[name], seed=71)
+    ref = reference(case)                    # the fused op's fp64 definition
+    g = ds.to_device(case, "cuda")
+    kw = dict(num_q_heads=case.Hq, num_kv_heads=case.Hkv, tokens_per_block=case.T, block_lens=g.block_lens,
+              scale=case.scale)
+    say(f"replaced path {name}")
+    if case.qknorm:
+        fused = drafter_attn_qknorm(g.qkv, g.k_pool, g.v_pool, g.page_table, g.context_lens, g.positions,
+                                    g.q_norm_weight, g.k_norm_weight, **kw)
+    else:
+        fused = drafter_attn(g.qkv, g.k_pool, g.v_pool, g.page_table, g.context_lens, **kw)
+    rows = g.qkv.clone()
+    if case.qknorm:
+        qk_norm_rope(rows, g.positions, g.q_norm_weight, g.k_norm_weight, num_q_heads=case.Hq,
+                     num_kv_heads=case.Hkv)
+    from speculative_decoding_drafter_amd import kv_append
+
+    kv_append(rows, g.k_pool, g.v_pool, g.page_table, g.context_lens, num_q_heads=case.Hq,
+              num_kv_heads=case.Hkv, tokens_per_block=case.T, block_lens=g.block_lens)
+    b = g.block_lens if g.block_lens is not None else torch.full_like(g.context_lens, case.T)
+    replaced = paged_attn(rows, g.k_pool, g.v_pool, g.page_table, g.context_lens + b, **kw)
+    check(to_np(replaced), ref, f"replaced-{name}")
+    check(to_np(fused), ref, f"fused-{name}")
+    # the two GPU paths agree to the same bar as each meets against fp64
+    check(to_np(replaced), to_np(fused), f"replaced-vs-fused-{name}")
+
+
+def test_replaced_path_long_context():
+    from speculative_decoding_drafter_amd import drafter_attn_qknorm, kv_append, paged_attn, qk_norm_rope
+
+    case = ds.with_append_room(ds.make_config(5), seed=72)     # one fresh page per request (513 per row)
+    g = ds.to_device(case, "cuda")
+    kw = dict(num_q_heads=case.Hq, num_kv_heads=case.Hkv, tokens_per_block=case.T, scale=case.scale)
+    say("replaced path, 32k contexts")
+    fused = drafter_attn_qknorm(g.qkv, g.k_pool, g.v_pool, g.page_table, g.context_lens, g.positions,
+                                g.q_norm_weight, g.k_norm_weight, **kw)
+    rows = g.qkv.clone()
+    qk_norm_rope(rows, g.positions, g.q_norm_weight, g.k_norm_weight, num_q_heads=case.Hq, num_kv_heads=case.Hkv)
+    kv_append(rows, g.k_pool, g.v_pool, g.page_table, g.context_lens, **kw_no_scale(kw))
+    replaced = paged_attn(rows, g.k_pool, g.v_pool, g.page_table, g.context_lens + case.T, **kw)
+    torch.cuda.synchronize()
+    check(to_np(replaced), to_np(fused), "replaced-vs-fused-32k")
+
+
+def kw_no_scale(kw):
+    return {k: v for k, v in kw.items() if k != "scale"}
+
+
+def test_paged_attn_zero_and_one_key():
+    from speculative_decoding_drafter_amd import paged_attn
+
+    case = ds.make_case(2, 4, 6, 1, [64, 5], seed=73, pool_pages=3)
+    g = ds.to_device(case, "cuda")
+    kw = dict(num_q_heads=6, num_kv_heads=1, tokens_per_block=4)
+    say("paged attention, 0 and 1 keys")
+    out0 = paged_attn(g.qkv, g.k_pool, g.v_pool, g.page_table, torch.zeros(2, dtype=torch.int32, device="cuda"), **kw)
+    out1 = paged_attn(g.qkv, g.k_pool, g.v_pool, g.page_table, torch.ones(2, dtype=torch.int32, device="cuda"), **kw)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out0) == 0
+    for r in range(2):
+        val = case.v_pool[int(case.page_table[r, 0]), 0, 0]
+        assert torch.equal(out1[r * 4:(r + 1) * 4].cpu().view(4, 6, 64), val.expand(4, 6, 64))
+
+
+def test_kv_append_flags_and_skips_bad_rows():
+    case = ds.with_append_room(ds.make_case(2, 4, 6, 1, [10, 62], seed=74, pool_pages=2), seed=75)
+    g = ds.to_device(case, "cuda")
+    before_k, before_v = g.k_pool.clone(), g.v_pool.clone()
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    # request 0: L + b beyond its row; request 1: the page of its second half out of range
+    g.context_lens[0] = case.stride * 64 - 2
+    g.page_table[1, 1] = case.num_pages + 5
+    say("append with bad rows")
+    _append_gpu(case, g, status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 1 | 2
+    changed = (g.k_pool != before_k).any(dim=(1, 2, 3)).nonzero().flatten().tolist()
+    # only request 1's first two tokens (slots 62, 63 of its first page) were written
+    assert changed == [int(case.page_table[1, 0])]
+    assert torch.equal(g.k_pool[changed[0], 0, :62], before_k[changed[0], 0, :62])
+    assert torch.equal(g.v_pool[changed[0], 0, 62:], g.qkv[4:6, 7 * 64:8 * 64])
