@@ -44,6 +44,10 @@ def parse():
     ap.add_argument("--cpu-budget-s", type=float, default=10.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 512 MiB device copy (for counter calibration)")
+    ap.add_argument("--ab-replaced", action="store_true",
+                    help="instead of the headline line: A/B of the fused call against the path it replaces "
+                         "(q/k norm + rotation, append to the pool, paged attention over L + b keys), "
+                         "interleaved, cold")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU run: turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, WRITE_SIZE) of a "
                          "--calibrate-copy run into profiles/traffic.json")
@@ -161,6 +165,98 @@ def write_traffic(fetch_csv: str, write_csv: str, workload: int):
     print(json.dumps(rec, indent=1))
 
 
+def ab_replaced(args):
+    """Fused op vs the path it replaces on the same workload (one fresh pool page per request
+    for the appended slots).  Each step is timed alone after the cache flush; the two are
+    interleaved in rounds so that both see the same machine state."""
+    import numpy as np
+    import torch
+
+    import drafter_synth as ds
+    from speculative_decoding_drafter_amd import (drafter_attn, drafter_attn_qknorm, kv_append, make_workspace,
+                                                  paged_attn, qk_norm_rope)
+
+    dev = torch.device("cuda:0")
+    case = ds.with_append_room(ds.make_config(args.config), seed=1000 * args.config + 7)
+    g = ds.to_device(case, dev)
+    ws = make_workspace(case.R, case.T, case.Hq, case.Hkv, case.stride, dev)
+    out = torch.empty(case.R * case.T, case.Hq * 64, dtype=torch.bfloat16, device=dev)
+    rows = g.qkv.clone()
+    b = g.block_lens if g.block_lens is not None else torch.full_like(g.context_lens, case.T)
+    kv_lens = g.context_lens + b
+    kw = dict(num_q_heads=case.Hq, num_kv_heads=case.Hkv, tokens_per_block=case.T, block_lens=g.block_lens)
+
+    def fused():
+        if case.qknorm:
+            drafter_attn_qknorm(g.qkv, g.k_pool, g.v_pool, g.page_table, g.context_lens, g.positions,
+                                g.q_norm_weight, g.k_norm_weight, scale=case.scale, out=out, workspace=ws, **kw)
+        else:
+            drafter_attn(g.qkv, g.k_pool, g.v_pool, g.page_table, g.context_lens, scale=case.scale, out=out,
+                         workspace=ws, **kw)
+
+    def stage_norm():
+        if case.qknorm:
+            qk_norm_rope(rows, g.positions, g.q_norm_weight, g.k_norm_weight, num_q_heads=case.Hq,
+                         num_kv_heads=case.Hkv)
+
+    def stage_append():
+        kv_append(rows, g.k_pool, g.v_pool, g.page_table, g.context_lens, **kw)
+
+    def stage_attn():
+        paged_attn(rows, g.k_pool, g.v_pool, g.page_table, kv_lens, scale=case.scale, out=out, workspace=ws, **kw)
+
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    flush_out = torch.empty((), dtype=torch.float32, device=dev)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    stages = [("append", stage_append), ("paged_attn", stage_attn)]
+    if case.qknorm:
+        stages.insert(0, ("norm", stage_norm))
+
+    def replaced():
+        for _, fn in stages:
+            fn()
+
+    # One event pair per timed interval (each pair adds its own overhead): the whole
+    # replaced path in one interval, and each of its stages alone in separate steps
+    # (the other stages run untimed around it).
+    variants = {"fused": [("fused", fused)], "replaced": [("replaced", replaced)],
+                "stages": [(name, fn) for name, fn in stages]}
+    res = {"fused": [], "replaced": []}
+    res.update({name: [] for name, _ in stages})
+    rounds = max(1, args.steps // 20)
+    for rnd in range(rounds + 1):              # round 0 is warm-up
+        order = ("fused", "replaced", "stages") if rnd % 2 else ("stages", "replaced", "fused")
+        for which in order:
+            for i in range(20):
+                if which == "stages":
+                    timed = stages[i % len(stages)][0]
+                    torch.sum(flush, dim=0, out=flush_out)
+                    e0, e1 = ev(), ev()
+                    for name, fn in stages:
+                        if name == timed:
+                            e0.record(); fn(); e1.record()
+                        else:
+                            fn()
+                else:
+                    timed, fn = variants[which][0]
+                    torch.sum(flush, dim=0, out=flush_out)
+                    e0, e1 = ev(), ev()
+                    e0.record(); fn(); e1.record()
+                torch.cuda.synchronize()
+                if rnd:
+                    res[timed].append(e0.elapsed_time(e1) * 1e3)
+    mean = {k: round(float(np.mean(v)), 3) for k, v in res.items()}
+    line = {"metric": "fused drafter attention vs the replaced path (us/call, cold)",
+            "fused_us": mean["fused"], "replaced_us": mean["replaced"],
+            "replaced_stages_us": {{"norm": "qk_norm_rope"}.get(k, "kv_append" if k == "append" else k): mean[k]
+                                   for k, _ in stages},
+            "replaced_over_fused": round(mean["replaced"] / mean["fused"], 4),
+            "steps_each": len(res["fused"]), "launches": {"fused": 1, "replaced": len(stages)},
+            "config": {"workload": WORKLOADS[args.config], "pool_pages": case.num_pages,
+                       "page_table_stride": case.stride}}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.traffic_from:
@@ -170,6 +266,9 @@ def main():
         print("bench.py runs on one GPU only: this hot path is not sharded across GPUs "
               "(see the design notes); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.ab_replaced:
+        ab_replaced(args)
+        return
     import torch
 
     import drafter_synth as ds
