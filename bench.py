@@ -148,7 +148,7 @@ def counter_means(path: str, counter: str):
     return {k: (sum(v) / len(v), len(v)) for k, v in out.items()}
 
 
-def write_traffic(fetch_csv: str, write_csv: str, workload: int):
+def write_traffic(fetch_csv: str, write_csv: str, workload: int, dest: str = None):
     fetch, write = counter_means(fetch_csv, "FETCH_SIZE"), counter_means(write_csv, "WRITE_SIZE")
     copy = next(k for k in fetch if "copyBuffer" in k)
     kern = next(k for k in fetch if "drafter_attn_kernel<" in k)
@@ -160,9 +160,10 @@ def write_traffic(fetch_csv: str, write_csv: str, workload: int):
            "copy_fetch_kib": fetch[copy][0], "copy_write_kib": write[copy][0],
            "fetch_scale": fs, "write_scale": ws,
            "traffic_bytes_per_launch": 1024 * (fetch[kern][0] * fs + write[kern][0] * ws)}
-    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
+    with open(dest or os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec, indent=1))
+    return rec
 
 
 def ab_replaced(args):
@@ -373,7 +374,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "traffic": None if args.hot else measured_traffic(args.config),
-                     "kernel": "drafter_attn_kernel<3,true,false>" if case.qknorm else "drafter_attn_kernel<3,false,false>"},
+                     "kernel": "drafter_attn_kernel<3,true,false,true>" if case.qknorm else "drafter_attn_kernel<3,false,false,true>"},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(case, args.cpu_budget_s)
