@@ -19,6 +19,11 @@
 // Nothing depends on device data except through loads, so the same launch is
 // valid for any rewritten lengths / page tables / qkv (graph replay), and the
 // split plan and every reduction order are fixed (bit-identical reruns).
+//
+// Also here: the standalone in-place q/k RMSNorm + NeoX rotation (the same
+// per-row arithmetic as the attention prologue), and, as a baseline for the
+// path the fused op replaces, the append of the block's K/V to the pool and the
+// attention kernel with the own-block path compiled out (pooled keys only).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
