@@ -110,9 +110,11 @@ size_t drafter_attn_workspace_bytes(int32_t num_requests, int32_t tokens_per_blo
 /*
  * The split-KV plan the library uses for these sizes: the page-table row is cut
  * into *num_splits ranges of *pages_per_split pages, each processed by one
- * workgroup.  It depends only on these host values (never on device data), so
- * results are bit-identical across reruns and graph replays.  Returns DA_OK or
- * DA_EINVAL.
+ * workgroup.  It depends only on these host values (never on device data).  On
+ * the device a request uses only the ranges its context length reaches (at
+ * least the first, which also holds the block's own keys), so the work follows
+ * the lengths while the same inputs always take the same path: results are
+ * bit-identical across reruns and graph replays.  Returns DA_OK or DA_EINVAL.
  */
 int drafter_attn_plan(int32_t num_requests, int32_t num_kv_heads, int32_t page_table_stride,
                       int32_t* num_splits, int32_t* pages_per_split);

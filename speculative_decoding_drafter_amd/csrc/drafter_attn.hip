@@ -4,9 +4,11 @@
 // include/drafter_attn.h.
 //
 // One launch per call.  Workgroup (split s, KV head g, request r), 8 waves:
-//   1. prologue: the 6*T query rows of group g (and, in the last split, the
-//      block's own K/V rows) go to LDS as bf16; in the qknorm variant each row
-//      is RMS-normalised and NeoX-rotated in fp32 on the way (angle in fp64).
+//   1. prologue: the 6*T query rows of group g (and, in split 0, the block's
+//      own K/V rows) go to LDS as bf16; in the qknorm variant each row is
+//      RMS-normalised and NeoX-rotated in fp32 on the way (angle in fp64).  A
+//      request uses only the splits its context reaches (read on the device);
+//      the workgroups of the others return at once.
 //   2. page loop: wave w walks pages s*Ps+w, +8, ... of the split.  Per page:
 //      the K and V tiles are copied HBM -> LDS by DMA (global_load_lds), S^T =
 //      K.Q^T with v_mfma_f32_16x16x32_bf16, online softmax in the exp2 domain,
@@ -15,7 +17,8 @@
 //   3. the 8 waves merge (max, sum, output) through LDS and write one fp32
 //      partial per workgroup;
 //   4. the last workgroup of each (r, g) (device-scope counter, reset by that
-//      workgroup) merges the splits in fixed order and writes bf16 output.
+//      workgroup) merges the splits in fixed order and writes bf16 output; a
+//      request that fits one split writes its output from that split directly.
 // Nothing depends on device data except through loads, so the same launch is
 // valid for any rewritten lengths / page tables / qkv (graph replay), and the
 // split plan and every reduction order are fixed (bit-identical reruns).
@@ -510,9 +513,9 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
   const int cand = first < row_end ? (row_end - first + kWaves - 1) / kWaves : 0;
   int id = 0;
   if (lane < cand) id = p.page_table[static_cast<int64_t>(r) * p.pt_stride + first + kWaves * lane];
-  const bool own = OWN && s == p.S - 1;
+  const bool own = OWN && s == 0;
   // Thread (sub, u) holds dims 8u .. 8u+7 of one head row: query row sub = 6t + h
-  // of the tile (sub < 6T), or, in the last split, row j < T of the block's own K
+  // of the tile (sub < 6T), or, in split 0, row j < T of the block's own K
   // (sub = 48 + j) or V (sub = 56 + j).  Rows past the block length are loaded
   // (they exist) and zeroed below.
   const int sub = tid >> 3, u = tid & 7;
@@ -550,6 +553,11 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
     b = b < 1 ? 1 : T;
   }
   const int npg = (L + kPage - 1) / kPage;
+  // Length-aware: a request uses only the splits its pages reach (at least split 0,
+  // which holds the block's own keys); its other workgroups have nothing to do.  A
+  // request that fits one split is answered by that split directly.
+  const int s_used = max(1, (npg + p.Ps - 1) / p.Ps);
+  if (s >= s_used) return;
   const int pend = min(npg, pbeg + p.Ps);
   // the block's own keys go to a wave with the fewest pages of this split
   const int own_wave = max(0, pend - pbeg) & (kWaves - 1);
@@ -737,7 +745,7 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
   const int t_row = row / kG;
   uint16_t* out_row = p.out + static_cast<int64_t>(r * T + t_row) * p.out_stride + (kG * g + row - kG * t_row) * kD +
                       4 * oc;
-  if (p.S == 1) {
+  if (s_used == 1) {
     // a single split: its merged state is the answer (l_wg > 0 unless there is no
     // key at all, possible only without the block's own keys: zero rows then)
     if (row_thread) {
@@ -770,19 +778,20 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
   int* last = reinterpret_cast<int*>(smem + kOffFlag);
   if (tid == 0) {
     const uint32_t prev = __hip_atomic_fetch_add(p.counters + rg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int is_last = (prev == static_cast<uint32_t>(p.S - 1));
+    const int is_last = (prev == static_cast<uint32_t>(s_used - 1));
     if (is_last) __hip_atomic_store(p.counters + rg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     *last = is_last;
   }
   __syncthreads();
   if (!*last || !row_thread) return;
 
-  // Thread (row, oc) merges its row's S partials in split order.  Memory round
-  // trips dominate here, so every load of a chunk of splits is issued before its
-  // first use: one round trip when S <= kChunk.
-  const int S = p.S;
-  const __amdgpu_buffer_rsrc_t pm = dev_rsrc(p.part_ml + static_cast<int64_t>(rg) * S * kRows * 2, S * kRows * 2 * 4);
-  const __amdgpu_buffer_rsrc_t po = dev_rsrc(p.part_o + static_cast<int64_t>(rg) * S * kRows * kD, S * kRows * kD * 4);
+  // Thread (row, oc) merges its row's S partials (the splits this request used) in
+  // split order.  Memory round trips dominate here, so every load of a chunk of
+  // splits is issued before its first use: one round trip when S <= kChunk.
+  const int S = s_used;
+  const int64_t slot0 = static_cast<int64_t>(rg) * p.S;  // the group's first partial slot
+  const __amdgpu_buffer_rsrc_t pm = dev_rsrc(p.part_ml + slot0 * kRows * 2, S * kRows * 2 * 4);
+  const __amdgpu_buffer_rsrc_t po = dev_rsrc(p.part_o + slot0 * kRows * kD, S * kRows * kD * 4);
   constexpr int kChunk = 8;
   f32x2 ml[kChunk];
   f32x4 ov[kChunk][2];
@@ -821,7 +830,7 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
       }
     }
   }
-  // den > 0 whenever there is a key (always with the block's own keys)
+  // den > 0 whenever there is a key (always with the block's own keys, in split 0)
   const float inv = den > 0.f ? 1.0f / den : 0.f;
   float x[8];
 #pragma unroll
