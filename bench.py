@@ -39,7 +39,8 @@ def parse():
     ap.add_argument("--hot", action="store_true", help="no cache flush between calls")
     ap.add_argument("--graph", action="store_true",
                     help="replay one call captured in a HIP graph instead of launching it directly "
-                         "(measured ~7.6 us slower per call between the events)")
+                         "(measured +7.2 us per call between the events with the runtime's default graph "
+                         "packet capture, +3.8 us with DEBUG_CLR_GRAPH_PACKET_CAPTURE=0 in the environment)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=10.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -358,7 +359,8 @@ def main():
         "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "kv_GBs_at_median": round(kv_bytes / (p50 * 1e-3) / 1e9, 2),
         "all_bytes_GBs": round((kv_bytes + other_bytes) / (mean_ms * 1e-3) / 1e9, 2),
-        "launch": "HIP graph replay" if args.graph else "direct",
+        "launch": ("HIP graph replay (DEBUG_CLR_GRAPH_PACKET_CAPTURE=%s)"
+                   % os.environ.get("DEBUG_CLR_GRAPH_PACKET_CAPTURE", "unset")) if args.graph else "direct",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
