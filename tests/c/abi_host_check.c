@@ -1,0 +1,27 @@
+/* A plain C99 caller of the C ABI (host-only queries, no device needed): the header
+ * must compile as C, and the library must answer its size and plan queries and
+ * reject out-of-contract calls with a message. */
+#include <stdio.h>
+#include <string.h>
+
+#include "drafter_attn.h"
+
+int main(void) {
+  int32_t splits = 0, pages = 0;
+  size_t ws = drafter_attn_workspace_bytes(8, 8, 24, 4, 512);
+  if (ws == 0 || ws % 256) { printf("bad workspace size %zu\n", ws); return 1; }
+  if (drafter_attn_plan(8, 4, 512, &splits, &pages) != DA_OK) { printf("plan failed\n"); return 1; }
+  if (splits < 1 || (size_t)splits * (size_t)pages < 512u) { printf("plan does not cover the row\n"); return 1; }
+  if (drafter_attn_workspace_bytes(9, 8, 6, 1, 4) != 0) { printf("R = 9 accepted\n"); return 1; }
+  /* an attention call that fails validation before any launch (head_dim 128) */
+  int rc = drafter_attn((const void*)0x10000, 512, (const void*)0x200000, (const void*)0x202000, 16384, 4,
+                        (const int32_t*)0x900000, 1, (const int32_t*)0x900100, NULL, 1, 8, 6, 1, 128, 64,
+                        0.125f, (void*)0xA00000, (size_t)1 << 20, (void*)0xB00000, 384, NULL, NULL);
+  if (rc != DA_EUNSUPPORTED || strlen(drafter_attn_last_error()) == 0) { printf("rc %d\n", rc); return 1; }
+  rc = drafter_qk_norm_rope((void*)0x10000, 512, 0, 6, 1, 64, (const void*)0x900000, DA_POS_INT32,
+                            (const void*)0x900100, (const void*)0x900200, 1e-5f, 10000.0f, NULL);
+  if (rc != DA_EINVAL) { printf("rc %d\n", rc); return 1; }
+  printf("ok splits=%d pages=%d workspace=%zu flags=%d,%d,%d\n", splits, pages, ws, DA_FLAG_CONTEXT_LEN,
+         DA_FLAG_PAGE_ID, DA_FLAG_BLOCK_LEN);
+  return 0;
+}
