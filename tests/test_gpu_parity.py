@@ -192,6 +192,22 @@ def test_large_stride_caps_pages_per_split():
     check(to_np(run(case)), reference(case), "stride4096")
 
 
+def test_contract_maximum_context():
+    # the longest row the contract allows: 16384 pages = 1,048,576 tokens (64 splits of 256
+    # pages, 32 per wave), next to an empty request
+    case = ds.make_case(2, 8, 6, 1, [16384 * 64, 0], seed=93, stride=16384, qknorm=True,
+                        pos_dtype=torch.int64)
+    say("contract maximum context (1M tokens)")
+    check(to_np(run(case)), reference(case), "ctx1M")
+
+
+def test_widest_head_layout_long_contexts():
+    # 8 requests x 8 tokens with 96 query / 16 KV heads and 16k-token contexts
+    case = ds.make_case(8, 8, 96, 16, [16384] * 7 + [16383], seed=94, qknorm=True)
+    say("96/16 heads, 16k contexts")
+    check(to_np(run(case)), reference(case), "h96x16")
+
+
 def test_status_flags_and_clamping():
     # device-value contract breaks are clamped (no out-of-range reads) and reported
     case = ds.make_case(2, 2, 6, 1, [100, 50], seed=5, stride=2, pool_pages=4)
