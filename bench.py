@@ -64,19 +64,13 @@ WORKLOADS = {
 }
 
 
-def cpu_baseline(case, budget_s: float):
-    """Time the fp64 oracle (as it stands) on a bounded sample of the same workload."""
-    import numpy as np
+def _oracle_rate(case, budget_s: float):
+    """K/V bytes per second of the fp64 oracle over whole requests, one at a time (cycling over
+    the batch), until the budget is used: (GB/s, request-passes, seconds)."""
     import oracle
 
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
     a = case.np_args()
     R = case.R
-    # sample: whole requests, one at a time (cycling over the batch), until the budget is used
     done_bytes = 0
     t0 = time.perf_counter()
     n_req = 0
@@ -96,9 +90,28 @@ def cpu_baseline(case, budget_s: float):
         if time.perf_counter() - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
-    return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{n_req} request-passes over the {R} requests of the same workload "
-                      f"(fp64 numpy oracle, {n_req / R:.2f} calls' worth), {dt:.1f} s"}
+    return done_bytes / dt / 1e9, n_req, dt
+
+
+def cpu_baseline(case, budget_s: float):
+    """Time the fp64 oracle (as it stands) on a bounded sample of the same workload: once with
+    the BLAS pool at its default size (the headline figure, ``cores`` = its threads) and once
+    with one thread."""
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads, threadpool_limits = 1, None
+    gbs, n_req, dt = _oracle_rate(case, budget_s)
+    out = {"value": round(gbs, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+           "sample": f"{n_req} request-passes over the {case.R} requests of the same workload "
+                     f"(fp64 numpy oracle, {n_req / case.R:.2f} calls' worth), {dt:.1f} s"}
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            gbs1, n1, dt1 = _oracle_rate(case, budget_s / 2)
+        out["one_thread"] = {"value": round(gbs1, 4), "unit": "GB/s", "cores": 1,
+                             "sample": f"{n1} request-passes, {dt1:.1f} s"}
+    return out
 
 
 KERNEL_SRC = os.path.join(ROOT, "speculative_decoding_drafter_amd", "csrc", "drafter_attn.hip")

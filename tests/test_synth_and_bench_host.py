@@ -85,3 +85,12 @@ def test_traffic_record_from_counter_csvs(tmp_path):
     assert rec["traffic_bytes_per_launch"] == 1024 * (200.0 * 2 + 20.0)
     assert json.load(open(out)) == rec
     assert rec["kernel_code_sha256"] == bench.kernel_code_hash()
+
+
+def test_cpu_baseline_reports_pool_and_one_thread():
+    import bench
+
+    case = ds.make_config(1)
+    rec = bench.cpu_baseline(case, 0.2)
+    assert rec["kind"] == "oracle" and rec["unit"] == "GB/s" and rec["value"] > 0 and rec["cores"] >= 1
+    assert rec["one_thread"]["cores"] == 1 and rec["one_thread"]["value"] > 0
