@@ -946,14 +946,17 @@ struct Plan {
 
 // Split plan from host-known sizes only.  Aim for about one workgroup per
 // compute unit over the whole (request, KV head, page) space, with a page count
-// per split that is a multiple of the 8 waves (small problems get fewer, fuller
-// workgroups rather than workgroups of idle waves); at most kMaxSplits splits.
+// per split that is a multiple of the 8 waves; at most kMaxSplits splits.  A
+// problem that small that a split would hold at most 4 pages' worth gets splits of
+// 4 pages (half the waves idle): a compute unit takes only a few of a workgroup's
+// page loads at a time, so twice the workgroups fetch the pages sooner, and the
+// combine then has no more than twice the partials to read.
 Plan make_plan(int R, int Hkv, int stride) {
   constexpr int kTargetWorkgroups = 256;
   if (stride <= 0) return {1, 1};
   const int64_t units = static_cast<int64_t>(R) * Hkv * stride;
   int ps = static_cast<int>((units + kTargetWorkgroups - 1) / kTargetWorkgroups);
-  ps = (ps + kWaves - 1) / kWaves * kWaves;  // >= one page per wave, a multiple of the waves
+  ps = ps <= 4 ? 4 : (ps + kWaves - 1) / kWaves * kWaves;
   if (ps > kMaxPagesPerSplit) ps = kMaxPagesPerSplit;
   int S = (stride + ps - 1) / ps;
   if (S > kMaxSplits) {

@@ -208,6 +208,30 @@ def test_widest_head_layout_long_contexts():
     check(to_np(run(case)), reference(case), "h96x16")
 
 
+def test_pages_beyond_2_31_elements_of_pool():
+    # with 96/16 heads a page is 128 KiB per pool: ids near 40,000 put a page 5.2 GB (2.6e9
+    # elements) into each pool, past any 32-bit element or byte offset; every other page is NaN
+    case = ds.make_case(2, 8, 96, 16, [300, 129], seed=95, qknorm=True, pool_pages=8)
+    g = ds.to_device(case, "cuda")
+    P = 40000
+    big_k = torch.full((P, 16, 64, 64), float("nan"), dtype=torch.bfloat16, device="cuda")
+    big_v = torch.full_like(big_k, float("nan"))
+    pt = g.page_table.clone()
+    k = 0
+    for r, L in enumerate(case.context_lens.tolist()):
+        for j in range(-(-L // 64)):
+            old, new = int(case.page_table[r, j]), P - 1 - 3 * k
+            big_k[new].copy_(g.k_pool[old])
+            big_v[new].copy_(g.v_pool[old])
+            pt[r, j] = new
+            k += 1
+    g.k_pool, g.v_pool, g.page_table = big_k, big_v, pt
+    say(f"pages up to id {P - 1} ({(P - 1) * 16 * 4096 * 2 / 1e9:.1f} GB into each pool)")
+    out = run(case, g)
+    del big_k, big_v
+    check(to_np(out), reference(case), "pool-beyond-2^31")
+
+
 def test_status_flags_and_clamping():
     # device-value contract breaks are clamped (no out-of-range reads) and reported
     case = ds.make_case(2, 2, 6, 1, [100, 50], seed=5, stride=2, pool_pages=4)
