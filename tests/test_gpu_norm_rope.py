@@ -73,6 +73,15 @@ def test_long_row_list_and_large_positions():
     _check_rows(rows, _apply(rows), "N4099")
 
 
+def test_int64_positions_beyond_int32():
+    # positions up to 2^33 (past the int32 range, and past fp32's 24-bit exact integers by
+    # 2^9): the angle is formed and reduced in fp64
+    rows = ds.make_norm_rope_rows(256, 4, seed=78, pos_dtype=torch.int64, pos_max=1 << 33)
+    assert int(rows.positions.max()) > 1 << 31
+    say("norm_rope int64 positions up to 2^33")
+    _check_rows(rows, _apply(rows), "pos2^33")
+
+
 def test_reruns_bit_identical():
     rows = ds.make_norm_rope_rows(64, 4, seed=9)
     a, b = _apply(rows), _apply(rows)

@@ -149,6 +149,14 @@ def test_qknorm_equals_cpu_norm_rope_then_plain():
     assert err.max() <= 2e-2 and err.mean() <= 1e-3
 
 
+def test_qknorm_int64_positions_beyond_int32():
+    # positions past the int32 range (up to 2^33 + L): the kernel forms and reduces the angle in fp64
+    case = ds.make_case(3, 8, 24, 4, [100, 700, 64], seed=96, qknorm=True, pos_dtype=torch.int64,
+                        pos_offset=[3_000_000_000, 1 << 33, 2 ** 31 + 5])
+    say("qknorm, int64 positions beyond 2^31")
+    check(to_np(run(case)), reference(case), "pos>2^31")
+
+
 def test_block_lens_and_layout_variants():
     # ragged blocks, separate pools, padded qkv rows (NaN padding), out with a wider row stride
     case = ds.make_case(5, 7, 24, 4, [0, 1, 64, 1999, 130], seed=23, block_lens=[7, 1, 3, 5, 2], qknorm=True,
