@@ -118,11 +118,15 @@ KERNEL_SRC = os.path.join(ROOT, "speculative_decoding_drafter_amd", "csrc", "dra
 
 
 def kernel_code_hash() -> str:
-    """sha256 of the kernel source with comments removed and whitespace collapsed: any change
-    to the code changes it, an edit of a comment does not."""
+    """sha256 of what decides a launch's memory traffic -- the device code (the source above its
+    host-side section) and the split plan (make_plan) -- with comments removed and whitespace
+    collapsed: any change to that code changes it; an edit of a comment or of host-side
+    validation does not."""
     import hashlib
     import re
-    text = open(KERNEL_SRC).read()
+    src = open(KERNEL_SRC).read()
+    plan = re.search(r"\nPlan make_plan\(.*?\n}\n", src, flags=re.S)
+    text = src.split("// host side", 1)[0] + (plan.group(0) if plan else "")
     text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
     text = re.sub(r"//[^\n]*", " ", text)
     text = " ".join(text.split())

@@ -122,7 +122,8 @@ int drafter_attn_plan(int32_t num_requests, int32_t num_kv_heads, int32_t page_t
 /*
  * k3_drafter_attn: q and the block's k are used as given (already normalised and
  * rotated).  scale must be finite and > 0 (usually 1/sqrt(64)).
- * Alignment: qkv, k_pool, v_pool and out 16-byte aligned; qkv_row_stride,
+ * Alignment: qkv, k_pool, v_pool and out 16-byte aligned; page_table,
+ * context_lens, block_lens and status_word 4-byte aligned; qkv_row_stride,
  * out_row_stride and pool_page_stride multiples of 8 elements.
  * out must not overlap any input or the workspace.
  */
@@ -147,7 +148,7 @@ int drafter_attn(const void* qkv, int64_t qkv_row_stride,
  * style: dims i and i+32 (i < 32) turn by pos * rope_base^(-2i/64) with pos =
  * positions[r*T+t].  The block's v and the paged context are not touched.
  * eps must be finite and >= 0, rope_base finite and > 0; positions_dtype is
- * DA_POS_INT32 or DA_POS_INT64.  The angle is formed and reduced in fp64, the
+ * DA_POS_INT32 or DA_POS_INT64, and positions aligned to its element size.  The angle is formed and reduced in fp64, the
  * rotation and the norm are computed in fp32, and q/k are rounded to bf16 once
  * before the contractions.
  */
@@ -182,7 +183,7 @@ int drafter_attn_qknorm(const void* qkv, int64_t qkv_row_stride,
  * bit-identical output to drafter_attn_qknorm on the original rows.
  *
  *   qkv        bf16 [num_tokens][qkv_row_stride] (device, read and written)
- *   positions  int32 or int64 [num_tokens] (device)
+ *   positions  int32 or int64 [num_tokens] (device, aligned to its element)
  *   q_norm_weight, k_norm_weight  bf16 [64] (device, 16-byte aligned)
  *
  * num_tokens in [1, DA_MAX_NORM_TOKENS]; num_q_heads = 6 * num_kv_heads,

@@ -989,6 +989,7 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned_to(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) & (n - 1)) == 0; }
 
 struct Common {
   const void* qkv;
@@ -1042,6 +1043,9 @@ int validate(const Common& a, size_t need_ws) {
   if (a.out_row_stride < static_cast<int64_t>(a.Hq) * kD) return fail(DA_EINVAL, "out_row_stride must be >= Hq * 64");
   if (a.out_row_stride % 8) return fail(DA_EINVAL, "out_row_stride must be a multiple of 8 elements");
   if (!aligned16(a.qkv) || !aligned16(a.out)) return fail(DA_EINVAL, "qkv and out must be 16-byte aligned");
+  if (!aligned_to(a.page_table, 4) || !aligned_to(a.context_lens, 4) || !aligned_to(a.block_lens, 4) ||
+      !aligned_to(a.status_word, 4))
+    return fail(DA_EINVAL, "page_table, context_lens, block_lens and status_word must be 4-byte aligned");
   if (!(std::isfinite(a.scale) && a.scale > 0.f)) return fail(DA_EINVAL, "scale must be finite and > 0");
   if (!a.workspace || a.workspace_bytes < need_ws)
     return fail(DA_EWORKSPACE, "workspace missing or smaller than drafter_attn_workspace_bytes()");
@@ -1188,6 +1192,8 @@ int drafter_attn_qknorm(const void* qkv, int64_t qkv_row_stride, const void* k_p
     return fail(DA_EINVAL, "positions, q_norm_weight and k_norm_weight must be non-NULL");
   if (positions_dtype != DA_POS_INT32 && positions_dtype != DA_POS_INT64)
     return fail(DA_EINVAL, "positions_dtype must be DA_POS_INT32 or DA_POS_INT64");
+  if (!aligned_to(positions, positions_dtype == DA_POS_INT64 ? 8 : 4))
+    return fail(DA_EINVAL, "positions must be aligned to its element size");
   if (!(std::isfinite(eps) && eps >= 0.f)) return fail(DA_EINVAL, "eps must be finite and >= 0");
   if (!(std::isfinite(rope_base) && rope_base > 0.f)) return fail(DA_EINVAL, "rope_base must be finite and > 0");
   if (!aligned16(q_norm_weight) || !aligned16(k_norm_weight))
@@ -1230,6 +1236,8 @@ int drafter_qk_norm_rope(void* qkv, int64_t qkv_row_stride, int32_t num_tokens, 
     return fail(DA_EINVAL, "qkv, q_norm_weight and k_norm_weight must be 16-byte aligned");
   if (positions_dtype != DA_POS_INT32 && positions_dtype != DA_POS_INT64)
     return fail(DA_EINVAL, "positions_dtype must be DA_POS_INT32 or DA_POS_INT64");
+  if (!aligned_to(positions, positions_dtype == DA_POS_INT64 ? 8 : 4))
+    return fail(DA_EINVAL, "positions must be aligned to its element size");
   if (!(std::isfinite(eps) && eps >= 0.f)) return fail(DA_EINVAL, "eps must be finite and >= 0");
   if (!(std::isfinite(rope_base) && rope_base > 0.f)) return fail(DA_EINVAL, "rope_base must be finite and > 0");
   const size_t qkv_n = static_cast<size_t>(((num_tokens - 1) * qkv_row_stride + width) * 2);
@@ -1290,6 +1298,9 @@ int drafter_kv_append(const void* qkv, int64_t qkv_row_stride, void* k_pool, voi
   if (pool_page_stride % 8) return fail(DA_EINVAL, "pool_page_stride must be a multiple of 8 elements");
   if (!aligned16(k_pool) || !aligned16(v_pool) || !aligned16(qkv))
     return fail(DA_EINVAL, "qkv, k_pool and v_pool must be 16-byte aligned");
+  if (!aligned_to(page_table, 4) || !aligned_to(context_lens, 4) || !aligned_to(block_lens, 4) ||
+      !aligned_to(status_word, 4))
+    return fail(DA_EINVAL, "page_table, context_lens, block_lens and status_word must be 4-byte aligned");
   const int64_t width = static_cast<int64_t>(num_q_heads + 2 * num_kv_heads) * kD;
   if (qkv_row_stride < width) return fail(DA_EINVAL, "qkv_row_stride must be >= (Hq + 2*Hkv) * 64");
   if (qkv_row_stride % 8) return fail(DA_EINVAL, "qkv_row_stride must be a multiple of 8 elements");

@@ -164,6 +164,8 @@ def test_qknorm_specific_checks(lib):
     assert q(eps=float("nan")) == DA_EINVAL
     assert q(base=0.0) == DA_EINVAL
     assert q(positions=0xB00000) == DA_EINVAL   # out overlaps positions
+    assert q(positions=0x900202) == DA_EINVAL and "aligned" in _lib.last_error()
+    assert q(positions=0x900204, pdt=1) == DA_EINVAL and "aligned" in _lib.last_error()
     assert q(R=9) == DA_EINVAL
 
 
@@ -248,3 +250,17 @@ def test_paged_attn_shares_the_attention_checks(lib):
     assert call(ws=0xA00010) == DA_EWORKSPACE
     assert call(out=0x10000 + 256) == DA_EINVAL
     assert call(qkv=0x10008) == DA_EINVAL
+
+
+def test_small_arrays_must_be_aligned_to_their_elements(lib):
+    # an int32 array or the status word (updated atomically) at an address that is not a
+    # multiple of 4, or int64 positions not on 8, is refused before any launch
+    for over in (dict(page_table=0x900002), dict(context_lens=0x900102), dict(block_lens=0x900202),
+                 dict(status=0x900302)):
+        assert _call(lib, **over) == DA_EINVAL, over
+        assert "aligned" in _lib.last_error()
+    for over in (dict(pt=0x900001), dict(cl=0x900103), dict(bl=0x900202), dict(st=0x900302)):
+        assert _ap(lib, **over) == DA_EINVAL, over
+        assert "aligned" in _lib.last_error()
+    assert _nr(lib, pos=0x900002) == DA_EINVAL and "aligned" in _lib.last_error()
+    assert _nr(lib, pos=0x900004, pdt=1) == DA_EINVAL and "aligned" in _lib.last_error()

@@ -94,3 +94,25 @@ def test_cpu_baseline_reports_pool_and_one_thread():
     rec = bench.cpu_baseline(case, 0.2)
     assert rec["kind"] == "oracle" and rec["unit"] == "GB/s" and rec["value"] > 0 and rec["cores"] >= 1
     assert rec["one_thread"]["cores"] == 1 and rec["one_thread"]["value"] > 0
+
+
+def test_traffic_record_key_follows_device_code_and_plan(tmp_path, monkeypatch):
+    # the record stays valid across host-side validation edits, not across device or plan edits
+    import bench
+
+    src = open(bench.KERNEL_SRC).read()
+    base = bench.kernel_code_hash()
+
+    def hash_of(text):
+        f = tmp_path / "k.hip"
+        f.write_text(text)
+        monkeypatch.setattr(bench, "KERNEL_SRC", str(f))
+        return bench.kernel_code_hash()
+
+    assert hash_of(src) == base
+    host_edit = src.replace('"qkv and out must be 16-byte aligned"', '"qkv and out: 16-byte alignment"')
+    assert host_edit != src and hash_of(host_edit) == base
+    device_edit = src.replace("kRescaleLog2 = 8", "kRescaleLog2 = 7")
+    assert device_edit != src and hash_of(device_edit) != base
+    plan_edit = src.replace("kTargetWorkgroups = 256", "kTargetWorkgroups = 512")
+    assert plan_edit != src and hash_of(plan_edit) != base
