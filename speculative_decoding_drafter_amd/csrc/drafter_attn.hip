@@ -61,11 +61,10 @@ constexpr int kOffOwnV = kOffOwnK + kMaxT * kD * 2;        // own block's V rows
 constexpr int kOffMW = kOffOwnV + kMaxT * kD * 2;          // [48][8] per-wave running max
 constexpr int kOffLW = kOffMW + kWaves * kRows * 4;        // [48][8] per-wave weight sum
 constexpr int kOffFlag = kOffLW + kWaves * kRows * 4;      // last-workgroup flag
-constexpr int kOffProg = kOffFlag + 16;                    // [8] pages done per wave
 constexpr int kOffStage = 14336;                           // [8 waves][K | V] page slots
 constexpr int kObufStride = kD + 4;  // after the loop a wave's slot holds its [48][68] fp32 output (pad: no bank conflicts)
 constexpr int kSmemBytes = kOffStage + kWaves * kStageBytes;
-static_assert(kOffProg + 4 * kWaves <= kOffStage, "LDS layout");
+static_assert(kOffFlag + 16 <= kOffStage, "LDS layout");
 // the own-block tiles are read like full 64-row tiles (rows past the block are
 // masked): their 8 KiB read windows must stay inside the allocation
 static_assert(kOffOwnV + kTileBytes <= kSmemBytes, "own-block read window");
@@ -618,13 +617,7 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
     stage_tile<false>(p.kpool + page_off(0), lds_k, doff);
     stage_tile<true>(p.vpool + page_off(0), lds_v, doff);
   }
-  // pages done per wave, read by the other wave of the SIMD.  Volatile keeps every
-  // access; the explicit LDS address space keeps them ds_read/ds_write (a generic
-  // volatile access would become a flat access that waits for the page DMA).
-  volatile __attribute__((address_space(3))) int* prog =
-      (volatile __attribute__((address_space(3))) int*)(smem + kOffProg);
-  if (tid < kWaves) prog[tid] = 0;
-  __syncthreads();
+  __syncthreads();  // the query tile, rotation table and own-block rows are in LDS
 
   const unsigned char* qt = smem + kOffQ;
   f32x4 o[NT][4];
@@ -649,14 +642,6 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
     const bool tail = cnt > 0 && first + kWaves * (cnt - 1) == npg - 1 && (L & (kPage - 1)) != 0;
     for (int i = 0; i < cnt; ++i) {
       const bool more = i + 1 < cnt;
-      // The two waves sharing a SIMD (w and w^4) get equal page counts, but issue
-      // arbitration favours the older one; the one that trails runs at raised
-      // priority.  Only the issue order changes, never which pages a wave owns.
-      if (lane == 0) prog[w] = i;
-      if (__builtin_amdgcn_readfirstlane(prog[w ^ 4]) > i)
-        __builtin_amdgcn_s_setprio(2);
-      else
-        __builtin_amdgcn_s_setprio(0);
       wait_vmcnt<8>();  // this page's K landed (its V may still be in flight)
       auto k_read = [&]() {
         if (more) {
@@ -678,7 +663,6 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
     }
   }
 
-  __builtin_amdgcn_s_setprio(0);
   // ---- merge the waves (fixed order).  Each wave leaves its running maxima and
   // sums and its unnormalised output in LDS -- the output inside its own page
   // slot, which it no longer reads -- and after one barrier each thread owns one
