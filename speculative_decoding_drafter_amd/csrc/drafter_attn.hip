@@ -574,7 +574,8 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
     return static_cast<int64_t>(__builtin_amdgcn_readlane(id, i)) * p.page_stride + head_off;
   };
   const DmaOffsets doff = dma_offsets(lane);
-  const bool early_dma = w >= kWaves - 2;  // no query rows: sub = 8w + lane/8 >= 48
+  // which waves issue their first page before their share of the prologue (see below)
+  const bool early_dma = w >= (p.Ps <= 2 * kWaves ? kWaves - 4 : kWaves - 2);
   if (early_dma && cnt > 0) {
     stage_tile<false>(p.kpool + page_off(0), lds_k, doff);
     stage_tile<true>(p.vpool + page_off(0), lds_v, doff);
@@ -606,13 +607,16 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
     *reinterpret_cast<u32x4*>(own_v ? smem + kOffOwnV + voff(oj, u) : smem + kOffOwnK + koff(oj, u)) =
         u32x4{0u, 0u, 0u, 0u};
   }
-  // Waves 0..5 issue their first page's DMA once their share of the prologue is
-  // done (the slots are not touched by the prologue).  A CU takes only about two
+  // The other waves issue their first page's DMA once their share of the prologue
+  // is done (the slots are not touched by the prologue).  A CU takes only about two
   // waves' worth of these 1 KiB DMAs at once; a wave issuing more waits until the
   // memory system drains, so a wave that issued before its prologue work would hold
   // the prologue back.  Waves 6 and 7, which hold no query rows, issue theirs
   // before the prologue: the stream starts early, and the other waves' first pages
   // are still in flight when the page loop starts and requests the second ones.
+  // With at most two pages per wave the loop is only a few round trips and the
+  // prologue is on the critical path, so waves 4 and 5 (the last 16 query rows)
+  // issue early too.
   if (!early_dma && cnt > 0) {
     stage_tile<false>(p.kpool + page_off(0), lds_k, doff);
     stage_tile<true>(p.vpool + page_off(0), lds_v, doff);
