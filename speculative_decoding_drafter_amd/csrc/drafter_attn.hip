@@ -501,15 +501,19 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
   // those loads from the DMA (issued from inline asm), so a load still pending
   // after it would wait for the whole page.
   //
-  // The page ids of this wave's pages of the split (pbeg+w, pbeg+w+8, ... -- at
-  // most 64, so one VGPR holds them and the page loop reads them with readlane,
+  // The page ids of this wave's pages of the split (every 8th page from `first` --
+  // at most 64, so one VGPR holds them and the page loop reads them with readlane,
   // with no memory access of its own) are loaded for the whole split range of the
   // row before the length is known; only the first cnt are used, checked and
   // clamped.
+  //
+  // A split narrower than the waves (4 pages) gives its pages to the highest
+  // waves, which have the least prologue work and issue their first page early.
   const int pbeg = s * p.Ps;
-  const int first = pbeg + w;
+  const int wshift = p.Ps < kWaves ? kWaves - p.Ps : 0;
+  const int first = pbeg + w - wshift;
   const int row_end = min(pbeg + p.Ps, p.pt_stride);
-  const int cand = first < row_end ? (row_end - first + kWaves - 1) / kWaves : 0;
+  const int cand = (w >= wshift && first < row_end) ? (row_end - first + kWaves - 1) / kWaves : 0;
   int id = 0;
   if (lane < cand) id = p.page_table[static_cast<int64_t>(r) * p.pt_stride + first + kWaves * lane];
   const bool own = OWN && s == 0;
@@ -559,8 +563,8 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
   if (s >= s_used) return;
   const int pend = min(npg, pbeg + p.Ps);
   // the block's own keys go to a wave with the fewest pages of this split
-  const int own_wave = max(0, pend - pbeg) & (kWaves - 1);
-  const int cnt = first < pend ? (pend - first + kWaves - 1) / kWaves : 0;
+  const int own_wave = (max(0, pend - pbeg) + wshift) & (kWaves - 1);
+  const int cnt = (w >= wshift && first < pend) ? (pend - first + kWaves - 1) / kWaves : 0;
   if (lane < cnt && (id < 0 || id >= p.num_pages)) {
     flag(p.status, DA_FLAG_PAGE_ID);
     id = id < 0 ? 0 : p.num_pages - 1;
