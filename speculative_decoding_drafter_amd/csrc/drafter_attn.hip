@@ -9,7 +9,8 @@
 //      RMS-normalised and NeoX-rotated in fp32 on the way (angle in fp64).  A
 //      request uses only the splits its context reaches (read on the device);
 //      the workgroups of the others return at once.
-//   2. page loop: wave w walks pages s*Ps+w, +8, ... of the split.  Per page:
+//   2. page loop: wave w walks every 8th page of the split from its w-th (a
+//      4-page split gives its pages to waves 4..7).  Per page:
 //      the K and V tiles are copied HBM -> LDS by DMA (global_load_lds), S^T =
 //      K.Q^T with v_mfma_f32_16x16x32_bf16, online softmax in the exp2 domain,
 //      V^T fragments by transposing LDS reads, O^T += V^T.P^T with MFMA.  The
@@ -125,10 +126,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
 }
 
-__device__ __forceinline__ uint16_t to_bf16(float x) {
-  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
-}
-
 __device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
@@ -220,10 +217,6 @@ __device__ __forceinline__ int key_of(int mt, int r16) {
   return 32 * (mt & 1) + 8 * (r16 & 3) + 4 * (mt >> 1) + (r16 >> 2);
 }
 
-// Stage one [64][64] bf16 tile (8 KiB contiguous in the pool) into LDS: 8 DMA
-// instructions, each reading 1 KiB (8 full rows) of global memory.  Lane l of
-// instruction jj writes row 8*jj + l/8, chunk column l%8, and reads the source
-// chunk the row's swizzle maps there.
 // Per-lane source offsets (bytes inside a tile) for stage_tile: DMA jj writes row
 // 8*jj + lane/8, chunk column lane%8; the source chunk is the one the row's swizzle
 // maps there.  Only jj % 4 matters, so 4 + 4 registers hold every offset.
@@ -420,8 +413,9 @@ __device__ __forceinline__ void flag(int32_t* status, int bit) {
 }
 
 // (cos, sin) of the NeoX angle pos * base^(-2i/64) for frequency i < 32: the angle
-// is formed and reduced modulo 2 pi in fp64 (exact enough for any position an
-// int64 can carry into the reduction), then evaluated in fp32.
+// is formed and reduced modulo 2 pi in fp64 (absolute error about |angle| * 2^-52,
+// 2e-6 rad at positions near 2^33, where fp32 could not even hold the position),
+// then evaluated in fp32.
 __device__ __forceinline__ float2 rope_cos_sin(int64_t pos, int i, double log2_base) {
   const double inv_freq = exp2(-static_cast<double>(i) * (1.0 / 32.0) * log2_base);  // base^(-2i/64)
   const double th = static_cast<double>(pos) * inv_freq;
@@ -939,7 +933,7 @@ struct Plan {
 // Split plan from host-known sizes only.  Aim for about one workgroup per
 // compute unit over the whole (request, KV head, page) space, with a page count
 // per split that is a multiple of the 8 waves; at most kMaxSplits splits.  A
-// problem that small that a split would hold at most 4 pages' worth gets splits of
+// problem so small that a split would hold at most 4 pages' worth gets splits of
 // 4 pages (half the waves idle): a compute unit takes only a few of a workgroup's
 // page loads at a time, so twice the workgroups fetch the pages sooner, and the
 // combine then has no more than twice the partials to read.
