@@ -41,6 +41,9 @@ def parse():
                     help="replay one call captured in a HIP graph instead of launching it directly "
                          "(measured +7.2 us per call between the events with the runtime's default graph "
                          "packet capture, +3.8 us with DEBUG_CLR_GRAPH_PACKET_CAPTURE=0 in the environment)")
+    ap.add_argument("--yarn", action="store_true",
+                    help="YaRN-scaled rotation (factor 4, 4096-token original context, ramp 1..32) in the qknorm "
+                         "call; reported beside the headline, not instead of it")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=10.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -301,10 +304,12 @@ def main():
     out = torch.empty(case.R * case.T, case.Hq * 64, dtype=torch.bfloat16, device=dev)
     kw = dict(num_q_heads=case.Hq, num_kv_heads=case.Hkv, tokens_per_block=case.T, scale=case.scale,
               out=out, workspace=ws)
+    yarn = dict(factor=4.0, original_max_position=4096, alpha=1.0, beta=32.0) if args.yarn else None
+    assert yarn is None or case.qknorm, "--yarn needs a qknorm workload"
     if case.qknorm:
         call = lambda: drafter_attn_qknorm(g.qkv, g.k_pool, g.v_pool, g.page_table, g.context_lens, g.positions,
                                            g.q_norm_weight, g.k_norm_weight, eps=case.eps,
-                                           rope_base=case.rope_base, **kw)
+                                           rope_base=case.rope_base, yarn=yarn, **kw)
     else:
         call = lambda: drafter_attn(g.qkv, g.k_pool, g.v_pool, g.page_table, g.context_lens, **kw)
 
@@ -376,6 +381,7 @@ def main():
         "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "kv_GBs_at_median": round(kv_bytes / (p50 * 1e-3) / 1e9, 2),
         "all_bytes_GBs": round((kv_bytes + other_bytes) / (mean_ms * 1e-3) / 1e9, 2),
+        "rope": "yarn factor 4, original context 4096, ramp 1..32" if yarn else "neox",
         "launch": ("HIP graph replay (DEBUG_CLR_GRAPH_PACKET_CAPTURE=%s)"
                    % os.environ.get("DEBUG_CLR_GRAPH_PACKET_CAPTURE", "unset")) if args.graph else "direct",
         "higher_is_better": True,

@@ -41,7 +41,8 @@
  *   positions  int32 or int64 [R*T], read per token (row order of qkv).
  *
  * Pointers: every array argument is a DEVICE pointer owned by the caller, except
- * that `stream` is a hipStream_t (NULL = the null stream).  The library
+ * that `stream` is a hipStream_t (NULL = the null stream) and `yarn` a host
+ * pointer to a small parameter struct read during the call.  The library
  * allocates nothing and never synchronises the host with the device: calls are
  * asynchronous in `stream` order and may be captured into a HIP graph.
  * The attention calls write only `out`, `workspace` and `status_word`; qkv, the
@@ -200,6 +201,61 @@ int drafter_qk_norm_rope(void* qkv, int64_t qkv_row_stride, int32_t num_tokens,
                          const void* q_norm_weight, const void* k_norm_weight,
                          float eps, float rope_base,
                          void* stream /* hipStream_t */);
+
+/*
+ * YaRN rotary scaling.  The drafter checkpoint is named with "YaRN 4.0" (page
+ * "K3 DFlash Sequence-Compaction GB300 Validation", Scope and results) and no
+ * other parameter, so the caller supplies them.  The method is the published one
+ * (Peng, Quesnelle, Fan, Shippole, "YaRN: Efficient Context Window Extension of
+ * Large Language Models", 2023, Section 3): for the frequency f_i = base^(-2i/64)
+ * of rotary pair i, turns = original_max_position * f_i / (2 pi) and
+ * gamma = clamp((turns - alpha) / (beta - alpha), 0, 1); the pair turns at
+ * (1 - gamma) * f_i / factor + gamma * f_i, and the rotated q and k are both
+ * multiplied by 0.1 * ln(factor) + 1 (the temperature: logits divided by t).
+ * factor 1 is the plain rotation, bit for bit.
+ */
+typedef struct da_yarn {
+  float factor;                  /* >= 1, finite ("YaRN 4.0": 4) */
+  int32_t original_max_position; /* >= 1: the context the base rotation was trained on */
+  float alpha;                   /* ramp start in turns, >= 0 (published: 1) */
+  float beta;                    /* ramp end in turns, > alpha (published: 32) */
+} da_yarn;
+
+/*
+ * drafter_attn_qknorm with YaRN-scaled rotation.  Arguments as drafter_attn_qknorm,
+ * plus `yarn` (a HOST pointer, read during the call; NULL = the plain rotation,
+ * i.e. drafter_attn_qknorm).  Out-of-range YaRN parameters return DA_EINVAL
+ * before any launch.
+ */
+int drafter_attn_qknorm_yarn(const void* qkv, int64_t qkv_row_stride,
+                             const void* k_pool, const void* v_pool, int64_t pool_page_stride,
+                             int32_t num_pages,
+                             const int32_t* page_table, int32_t page_table_stride,
+                             const int32_t* context_lens, const int32_t* block_lens,
+                             int32_t num_requests, int32_t tokens_per_block,
+                             int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t page_size,
+                             float scale,
+                             const void* positions, int32_t positions_dtype,
+                             const void* q_norm_weight, const void* k_norm_weight,
+                             float eps, float rope_base, const da_yarn* yarn,
+                             void* workspace, size_t workspace_bytes,
+                             void* out, int64_t out_row_stride,
+                             int32_t* status_word,
+                             void* stream);
+
+/*
+ * drafter_qk_norm_rope with YaRN-scaled rotation (same arithmetic as
+ * drafter_attn_qknorm_yarn's prologue, so drafter_attn on rows processed here
+ * equals drafter_attn_qknorm_yarn on the original rows, bit for bit).  `yarn` as
+ * there (host pointer, NULL = plain).
+ */
+int drafter_qk_norm_rope_yarn(void* qkv, int64_t qkv_row_stride, int32_t num_tokens,
+                              int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                              const void* positions, int32_t positions_dtype,
+                              const void* q_norm_weight, const void* k_norm_weight,
+                              float eps, float rope_base, const da_yarn* yarn,
+                              void* stream /* hipStream_t */);
 
 /*
  * The path the fused op replaces, built here as an A/B baseline (TensorRT-LLM PR

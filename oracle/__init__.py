@@ -9,6 +9,8 @@ from .drafter_attn_oracle import (  # noqa: F401
     rms_norm,
     rope_neox,
     rope_inv_freq,
+    yarn_inv_freq,
+    yarn_mscale,
     gather_context,
     drafter_attn,
     drafter_attn_qknorm,

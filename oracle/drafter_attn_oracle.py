@@ -73,19 +73,53 @@ def rope_inv_freq(base: float, dim: int = HEAD_DIM) -> np.ndarray:
     return np.power(float(base), -2.0 * i / dim)
 
 
-def rope_neox(x: np.ndarray, pos, base: float) -> np.ndarray:
+def yarn_inv_freq(base: float, factor: float, original_max_position: int, alpha: float = 1.0,
+                  beta: float = 32.0, dim: int = HEAD_DIM) -> np.ndarray:
+    """YaRN's frequencies ("NTK-by-parts"), for the drafter checkpoint's "YaRN 4.0".
+
+    The drafter line of "K3 DFlash Sequence-Compaction GB300 Validation" (Scope and
+    results) names YaRN with factor 4.0 and no other parameter; the method is the
+    published one (Peng, Quesnelle, Fan, Shippole, "YaRN: Efficient Context Window
+    Extension of Large Language Models", 2023, Section 3): for rotary pair ``i`` with
+    base frequency ``theta``, the number of turns it makes over the original context
+    is ``r = L * theta / (2 pi)``; ``gamma(r)`` is 0 below ``alpha``, 1 above
+    ``beta`` and linear in ``r`` between them; the new frequency is
+    ``(1 - gamma) * theta / s + gamma * theta``: pairs that turn many times keep their
+    frequency, pairs that turn less than ``alpha`` times are interpolated by ``s``.
+    """
+    theta = rope_inv_freq(base, dim)
+    turns = float(original_max_position) * theta / (2.0 * math.pi)
+    gamma = np.clip((turns - alpha) / (beta - alpha), 0.0, 1.0)
+    return (1.0 - gamma) * theta / float(factor) + gamma * theta
+
+
+def yarn_mscale(factor: float) -> float:
+    """YaRN's attention temperature as a factor on q and on k: ``sqrt(1/t) = 0.1 ln(s) + 1``
+    (the same paper, Section 3.4), so the logits are divided by ``t``."""
+    return 0.1 * math.log(float(factor)) + 1.0
+
+
+def rope_neox(x: np.ndarray, pos, base: float, yarn: Optional[dict] = None) -> np.ndarray:
     """NeoX ("rotate half") rotary embedding over the last axis.
 
     PR #20532, fused_qk_norm_rope drafter cell: NeoX style, base 10000.
     Dimension ``i`` pairs with ``i + dim/2``; the pair is turned by the angle
-    ``pos * inv_freq[i]``.  ``pos`` broadcasts against ``x[..., 0]``.
+    ``pos * inv_freq[i]``.  ``pos`` broadcasts against ``x[..., 0]``.  With
+    ``yarn`` (``factor``, ``original_max_position``, optional ``alpha``, ``beta``)
+    the frequencies are YaRN's and the rotated vector is scaled by ``yarn_mscale``.
     """
     x = np.asarray(x, dtype=np.float64)
     half = x.shape[-1] // 2
-    ang = np.asarray(pos, dtype=np.float64)[..., None] * rope_inv_freq(base, x.shape[-1])
+    if yarn is None:
+        inv_freq, m = rope_inv_freq(base, x.shape[-1]), 1.0
+    else:
+        inv_freq = yarn_inv_freq(base, yarn["factor"], yarn["original_max_position"], yarn.get("alpha", 1.0),
+                                 yarn.get("beta", 32.0), x.shape[-1])
+        m = yarn_mscale(yarn["factor"])
+    ang = np.asarray(pos, dtype=np.float64)[..., None] * inv_freq
     c, s = np.cos(ang), np.sin(ang)
     x1, x2 = x[..., :half], x[..., half:]
-    return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
+    return m * np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
 
 
 # --------------------------------------------------------------------------------------
@@ -222,12 +256,12 @@ def drafter_attn(qkv, k_pool, v_pool, page_table, context_lens, block_lens=None,
 def drafter_attn_qknorm(qkv, k_pool, v_pool, page_table, context_lens, block_lens=None, *,
                         positions, q_norm_weight, k_norm_weight, num_q_heads: int,
                         num_kv_heads: int, tokens_per_block: int, scale: Optional[float] = None,
-                        eps: float = 1e-5, rope_base: float = 10000.0,
+                        eps: float = 1e-5, rope_base: float = 10000.0, yarn: Optional[dict] = None,
                         return_probs: bool = False, **_unused):
     """k3_drafter_attn_qknorm: RMSNorm then NeoX RoPE on the block's q and k, then attention.
 
     The block's v and the whole paged context are used as stored.  Positions
-    are read per token (``positions[r*T + t]``).
+    are read per token (``positions[r*T + t]``).  ``yarn``: see ``rope_neox``.
     """
     if scale is None:
         scale = 1.0 / math.sqrt(HEAD_DIM)
@@ -236,7 +270,7 @@ def drafter_attn_qknorm(qkv, k_pool, v_pool, page_table, context_lens, block_len
 
     def prep(w):
         def f(x, r, b):
-            return rope_neox(rms_norm(x, w, eps), pos[r * T:r * T + b], rope_base)
+            return rope_neox(rms_norm(x, w, eps), pos[r * T:r * T + b], rope_base, yarn)
         return f
 
     return _run(qkv, k_pool, v_pool, page_table, context_lens, block_lens, num_q_heads,
@@ -244,7 +278,8 @@ def drafter_attn_qknorm(qkv, k_pool, v_pool, page_table, context_lens, block_len
 
 
 def qk_norm_rope(qkv, positions, q_norm_weight, k_norm_weight, *, num_q_heads: int,
-                 num_kv_heads: int, eps: float = 1e-5, rope_base: float = 10000.0) -> np.ndarray:
+                 num_kv_heads: int, eps: float = 1e-5, rope_base: float = 10000.0,
+                 yarn: Optional[dict] = None) -> np.ndarray:
     """fused_qk_norm_rope, the drafter's cell, on packed qkv rows.
 
     PR #20532, commit adding fused_qk_norm_rope's drafter cell (head_dim 64,
@@ -264,10 +299,10 @@ def qk_norm_rope(qkv, positions, q_norm_weight, k_norm_weight, *, num_q_heads: i
         raise OracleContractError("qkv narrower than its heads, or not 6 query heads per KV head")
     for h in range(Hq):
         c = q_cols(h, Hq, Hkv)
-        x[:, c] = rope_neox(rms_norm(x[:, c], q_norm_weight, eps), pos, rope_base)
+        x[:, c] = rope_neox(rms_norm(x[:, c], q_norm_weight, eps), pos, rope_base, yarn)
     for g in range(Hkv):
         c = k_cols(g, Hq, Hkv)
-        x[:, c] = rope_neox(rms_norm(x[:, c], k_norm_weight, eps), pos, rope_base)
+        x[:, c] = rope_neox(rms_norm(x[:, c], k_norm_weight, eps), pos, rope_base, yarn)
     return x
 
 

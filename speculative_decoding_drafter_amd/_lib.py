@@ -10,6 +10,15 @@ _lib = None
 c_i32, c_i64, c_f32, c_sz, c_vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
 c_i32p = ctypes.POINTER(ctypes.c_int32)
 
+
+class DaYarn(ctypes.Structure):
+    """struct da_yarn of the header (YaRN rotary scaling parameters, passed by host pointer)."""
+    _fields_ = [("factor", ctypes.c_float), ("original_max_position", ctypes.c_int32),
+                ("alpha", ctypes.c_float), ("beta", ctypes.c_float)]
+
+
+c_yarnp = ctypes.POINTER(DaYarn)
+
 # name -> (restype, argtypes), in the header's order
 SIGNATURES = {
     "drafter_attn_workspace_bytes": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32]),
@@ -41,6 +50,21 @@ SIGNATURES = {
         c_vp, c_i64,
         c_vp, c_vp,
     ]),
+    "drafter_attn_qknorm_yarn": (ctypes.c_int, [
+        c_vp, c_i64,
+        c_vp, c_vp, c_i64, c_i32,
+        c_vp, c_i32,
+        c_vp, c_vp,
+        c_i32, c_i32, c_i32, c_i32,
+        c_i32, c_i32,
+        c_f32,
+        c_vp, c_i32,
+        c_vp, c_vp,
+        c_f32, c_f32, c_yarnp,        # eps, rope_base, yarn (host struct)
+        c_vp, c_sz,
+        c_vp, c_i64,
+        c_vp, c_vp,
+    ]),
     "drafter_qk_norm_rope": (ctypes.c_int, [
         c_vp, c_i64, c_i32,           # qkv, qkv_row_stride, num_tokens
         c_i32, c_i32, c_i32,          # Hq, Hkv, head_dim
@@ -48,6 +72,14 @@ SIGNATURES = {
         c_vp, c_vp,                   # q_norm_weight, k_norm_weight
         c_f32, c_f32,                 # eps, rope_base
         c_vp,                         # stream
+    ]),
+    "drafter_qk_norm_rope_yarn": (ctypes.c_int, [
+        c_vp, c_i64, c_i32,
+        c_i32, c_i32, c_i32,
+        c_vp, c_i32,
+        c_vp, c_vp,
+        c_f32, c_f32, c_yarnp,        # eps, rope_base, yarn (host struct)
+        c_vp,
     ]),
     "drafter_kv_append": (ctypes.c_int, [
         c_vp, c_i64,                  # qkv, qkv_row_stride

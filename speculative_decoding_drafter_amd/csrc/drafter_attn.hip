@@ -81,6 +81,18 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// Rotary parameters: frequencies base^(-2i/64), optionally rescaled by YaRN (its
+// "NTK-by-parts" frequencies and a temperature factor on q and on k).
+struct Rope {
+  double log2_base;   // log2(rope_base)
+  double turn_scale;  // YaRN: L / (2 pi) -- turns of a frequency over the original context L
+  double alpha;       // YaRN ramp start (turns)
+  double inv_ramp;    // YaRN: 1 / (beta - alpha)
+  double inv_s;       // YaRN: 1 / factor
+  float mscale;       // YaRN: 0.1 ln(factor) + 1, applied to cos and sin
+  int32_t yarn;       // 0: plain frequencies, no temperature factor
+};
+
 struct Params {
   const uint16_t* qkv;
   int64_t qkv_stride;
@@ -105,7 +117,7 @@ struct Params {
   int32_t S, Ps;
   float c;    // scale * log2(e): scores live in the exp2 domain
   float eps;
-  double log2_base;  // log2(rope_base), fp64
+  Rope rope;
 };
 
 // ---------------------------------------------------------------------------------
@@ -412,17 +424,28 @@ __device__ __forceinline__ void flag(int32_t* status, int bit) {
   if (status) atomicOr(status, bit);
 }
 
-// (cos, sin) of the NeoX angle pos * base^(-2i/64) for frequency i < 32: the angle
-// is formed and reduced modulo 2 pi in fp64 (absolute error about |angle| * 2^-52,
-// 2e-6 rad at positions near 2^33, where fp32 could not even hold the position),
-// then evaluated in fp32.
-__device__ __forceinline__ float2 rope_cos_sin(int64_t pos, int i, double log2_base) {
-  const double inv_freq = exp2(-static_cast<double>(i) * (1.0 / 32.0) * log2_base);  // base^(-2i/64)
+// (cos, sin) of the NeoX angle pos * f_i for frequency i < 32, f_i = base^(-2i/64):
+// the angle is formed and reduced modulo 2 pi in fp64 (absolute error about
+// |angle| * 2^-52, 2e-6 rad at positions near 2^33, where fp32 could not even hold
+// the position), then evaluated in fp32.  With YaRN, f_i is first moved towards
+// f_i / s by gamma = clamp((turns - alpha) / (beta - alpha), 0, 1) of its turns over
+// the original context (f_i <- (1 - gamma) f_i / s + gamma f_i), and cos and sin
+// carry the temperature factor.
+__device__ __forceinline__ float2 rope_cos_sin(int64_t pos, int i, const Rope& rp) {
+  double inv_freq = exp2(-static_cast<double>(i) * (1.0 / 32.0) * rp.log2_base);  // base^(-2i/64)
+  if (rp.yarn) {
+    const double g = fmin(fmax((rp.turn_scale * inv_freq - rp.alpha) * rp.inv_ramp, 0.0), 1.0);
+    inv_freq = (1.0 - g) * inv_freq * rp.inv_s + g * inv_freq;
+  }
   const double th = static_cast<double>(pos) * inv_freq;
   const double kq = rint(th * 0.15915494309189535);    // 1 / (2 pi)
   const double red = fma(-kq, 6.283185307179586, th);  // |red| <= pi (+ tiny)
   float sn, cn;
   sincosf(static_cast<float>(red), &sn, &cn);
+  if (rp.yarn) {
+    sn *= rp.mscale;
+    cn *= rp.mscale;
+  }
   return make_float2(cn, sn);
 }
 
@@ -582,7 +605,7 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
   float2* cs = reinterpret_cast<float2*>(smem + kOffCS);
   // ---- a2/a3 (qknorm): rotation table, one (token, frequency) per thread
   if (QKNORM) {
-    if (tid < T * 32) cs[tid] = rope_cos_sin(pos, tid & 31, p.log2_base);
+    if (tid < T * 32) cs[tid] = rope_cos_sin(pos, tid & 31, p.rope);
     __syncthreads();
   }
 
@@ -845,7 +868,7 @@ struct NrParams {
   const uint16_t* wk;
   int32_t N, Hq, Hkv;
   float eps;
-  double log2_base;
+  Rope rope;
 };
 
 template <bool POS64>
@@ -868,7 +891,7 @@ __global__ __launch_bounds__(kNrThreads) void qk_norm_rope_kernel(const NrParams
   if (tid < nt * 32)
     pos = POS64 ? static_cast<const int64_t*>(p.positions)[t0 + (tid >> 5)]
                 : static_cast<int64_t>(static_cast<const int32_t*>(p.positions)[t0 + (tid >> 5)]);
-  if (tid < nt * 32) cs[tid] = rope_cos_sin(pos, tid & 31, p.log2_base);
+  if (tid < nt * 32) cs[tid] = rope_cos_sin(pos, tid & 31, p.rope);
   __syncthreads();
   if (live) {
     float x[8];
@@ -1116,6 +1139,34 @@ int launch_norm_rope(const NrParams& p, hipStream_t stream) {
   return DA_OK;
 }
 
+int check_yarn(const da_yarn* y) {
+  if (!y) return DA_OK;
+  if (!(std::isfinite(y->factor) && y->factor >= 1.f)) return fail(DA_EINVAL, "yarn factor must be finite and >= 1");
+  if (y->original_max_position < 1) return fail(DA_EINVAL, "yarn original_max_position must be >= 1");
+  if (!(std::isfinite(y->alpha) && std::isfinite(y->beta) && y->alpha >= 0.f && y->beta > y->alpha))
+    return fail(DA_EINVAL, "yarn alpha and beta must be finite with 0 <= alpha < beta");
+  return DA_OK;
+}
+
+// The rotation's parameters from the host arguments.  A YaRN factor of 1 is the
+// plain rotation (taken as such, so it gives the same bits).
+Rope make_rope(float rope_base, const da_yarn* y) {
+  Rope r;
+  std::memset(&r, 0, sizeof(r));
+  r.log2_base = std::log2(static_cast<double>(rope_base));
+  r.inv_s = 1.0;
+  r.mscale = 1.f;
+  if (y && y->factor != 1.f) {
+    r.yarn = 1;
+    r.turn_scale = static_cast<double>(y->original_max_position) / 6.283185307179586;  // L / (2 pi)
+    r.alpha = y->alpha;
+    r.inv_ramp = 1.0 / (static_cast<double>(y->beta) - static_cast<double>(y->alpha));
+    r.inv_s = 1.0 / static_cast<double>(y->factor);
+    r.mscale = static_cast<float>(0.1 * std::log(static_cast<double>(y->factor)) + 1.0);
+  }
+  return r;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1158,15 +1209,15 @@ int drafter_attn(const void* qkv, int64_t qkv_row_stride, const void* k_pool, co
   return launch_nt<false, false>(p, plan, static_cast<hipStream_t>(stream));
 }
 
-int drafter_attn_qknorm(const void* qkv, int64_t qkv_row_stride, const void* k_pool, const void* v_pool,
-                        int64_t pool_page_stride, int32_t num_pages, const int32_t* page_table,
-                        int32_t page_table_stride, const int32_t* context_lens, const int32_t* block_lens,
-                        int32_t num_requests, int32_t tokens_per_block, int32_t num_q_heads,
-                        int32_t num_kv_heads, int32_t head_dim, int32_t page_size, float scale,
-                        const void* positions, int32_t positions_dtype, const void* q_norm_weight,
-                        const void* k_norm_weight, float eps, float rope_base, void* workspace,
-                        size_t workspace_bytes, void* out, int64_t out_row_stride, int32_t* status_word,
-                        void* stream) {
+int drafter_attn_qknorm_yarn(const void* qkv, int64_t qkv_row_stride, const void* k_pool, const void* v_pool,
+                             int64_t pool_page_stride, int32_t num_pages, const int32_t* page_table,
+                             int32_t page_table_stride, const int32_t* context_lens, const int32_t* block_lens,
+                             int32_t num_requests, int32_t tokens_per_block, int32_t num_q_heads,
+                             int32_t num_kv_heads, int32_t head_dim, int32_t page_size, float scale,
+                             const void* positions, int32_t positions_dtype, const void* q_norm_weight,
+                             const void* k_norm_weight, float eps, float rope_base, const da_yarn* yarn,
+                             void* workspace, size_t workspace_bytes, void* out, int64_t out_row_stride,
+                             int32_t* status_word, void* stream) {
   const Common a{qkv, qkv_row_stride, k_pool, v_pool, pool_page_stride, num_pages, page_table, page_table_stride,
                  context_lens, block_lens, num_requests, tokens_per_block, num_q_heads, num_kv_heads, head_dim,
                  page_size, scale, workspace, workspace_bytes, out, out_row_stride, status_word, stream};
@@ -1182,6 +1233,8 @@ int drafter_attn_qknorm(const void* qkv, int64_t qkv_row_stride, const void* k_p
     return fail(DA_EINVAL, "positions must be aligned to its element size");
   if (!(std::isfinite(eps) && eps >= 0.f)) return fail(DA_EINVAL, "eps must be finite and >= 0");
   if (!(std::isfinite(rope_base) && rope_base > 0.f)) return fail(DA_EINVAL, "rope_base must be finite and > 0");
+  rc = check_yarn(yarn);
+  if (rc != DA_OK) return rc;
   if (!aligned16(q_norm_weight) || !aligned16(k_norm_weight))
     return fail(DA_EINVAL, "q_norm_weight and k_norm_weight must be 16-byte aligned");
   const int64_t rows = static_cast<int64_t>(num_requests) * tokens_per_block;
@@ -1199,16 +1252,32 @@ int drafter_attn_qknorm(const void* qkv, int64_t qkv_row_stride, const void* k_p
   p.wq = static_cast<const uint16_t*>(q_norm_weight);
   p.wk = static_cast<const uint16_t*>(k_norm_weight);
   p.eps = eps;
-  p.log2_base = std::log2(static_cast<double>(rope_base));
+  p.rope = make_rope(rope_base, yarn);
   g_last_error.clear();
   hipStream_t st = static_cast<hipStream_t>(stream);
   return positions_dtype == DA_POS_INT64 ? launch_nt<true, true>(p, plan, st) : launch_nt<true, false>(p, plan, st);
 }
 
-int drafter_qk_norm_rope(void* qkv, int64_t qkv_row_stride, int32_t num_tokens, int32_t num_q_heads,
-                         int32_t num_kv_heads, int32_t head_dim, const void* positions, int32_t positions_dtype,
-                         const void* q_norm_weight, const void* k_norm_weight, float eps, float rope_base,
-                         void* stream) {
+int drafter_attn_qknorm(const void* qkv, int64_t qkv_row_stride, const void* k_pool, const void* v_pool,
+                        int64_t pool_page_stride, int32_t num_pages, const int32_t* page_table,
+                        int32_t page_table_stride, const int32_t* context_lens, const int32_t* block_lens,
+                        int32_t num_requests, int32_t tokens_per_block, int32_t num_q_heads,
+                        int32_t num_kv_heads, int32_t head_dim, int32_t page_size, float scale,
+                        const void* positions, int32_t positions_dtype, const void* q_norm_weight,
+                        const void* k_norm_weight, float eps, float rope_base, void* workspace,
+                        size_t workspace_bytes, void* out, int64_t out_row_stride, int32_t* status_word,
+                        void* stream) {
+  return drafter_attn_qknorm_yarn(qkv, qkv_row_stride, k_pool, v_pool, pool_page_stride, num_pages, page_table,
+                                  page_table_stride, context_lens, block_lens, num_requests, tokens_per_block,
+                                  num_q_heads, num_kv_heads, head_dim, page_size, scale, positions,
+                                  positions_dtype, q_norm_weight, k_norm_weight, eps, rope_base, nullptr,
+                                  workspace, workspace_bytes, out, out_row_stride, status_word, stream);
+}
+
+int drafter_qk_norm_rope_yarn(void* qkv, int64_t qkv_row_stride, int32_t num_tokens, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t head_dim, const void* positions,
+                              int32_t positions_dtype, const void* q_norm_weight, const void* k_norm_weight,
+                              float eps, float rope_base, const da_yarn* yarn, void* stream) {
   if (head_dim != kD) return fail(DA_EUNSUPPORTED, "head_dim must be 64");
   if (num_kv_heads < 1 || num_kv_heads > DA_MAX_KV_HEADS) return fail(DA_EINVAL, "num_kv_heads must be in [1, 16]");
   if (num_q_heads != kG * num_kv_heads) return fail(DA_EUNSUPPORTED, "num_q_heads must be 6 * num_kv_heads");
@@ -1226,6 +1295,8 @@ int drafter_qk_norm_rope(void* qkv, int64_t qkv_row_stride, int32_t num_tokens, 
     return fail(DA_EINVAL, "positions must be aligned to its element size");
   if (!(std::isfinite(eps) && eps >= 0.f)) return fail(DA_EINVAL, "eps must be finite and >= 0");
   if (!(std::isfinite(rope_base) && rope_base > 0.f)) return fail(DA_EINVAL, "rope_base must be finite and > 0");
+  const int rc = check_yarn(yarn);
+  if (rc != DA_OK) return rc;
   const size_t qkv_n = static_cast<size_t>(((num_tokens - 1) * qkv_row_stride + width) * 2);
   const size_t pos_n = static_cast<size_t>(num_tokens) * (positions_dtype == DA_POS_INT64 ? 8 : 4);
   if (overlaps(qkv, qkv_n, positions, pos_n) || overlaps(qkv, qkv_n, q_norm_weight, kD * 2) ||
@@ -1242,10 +1313,18 @@ int drafter_qk_norm_rope(void* qkv, int64_t qkv_row_stride, int32_t num_tokens, 
   p.Hq = num_q_heads;
   p.Hkv = num_kv_heads;
   p.eps = eps;
-  p.log2_base = std::log2(static_cast<double>(rope_base));
+  p.rope = make_rope(rope_base, yarn);
   g_last_error.clear();
   hipStream_t st = static_cast<hipStream_t>(stream);
   return positions_dtype == DA_POS_INT64 ? launch_norm_rope<true>(p, st) : launch_norm_rope<false>(p, st);
+}
+
+int drafter_qk_norm_rope(void* qkv, int64_t qkv_row_stride, int32_t num_tokens, int32_t num_q_heads,
+                         int32_t num_kv_heads, int32_t head_dim, const void* positions, int32_t positions_dtype,
+                         const void* q_norm_weight, const void* k_norm_weight, float eps, float rope_base,
+                         void* stream) {
+  return drafter_qk_norm_rope_yarn(qkv, qkv_row_stride, num_tokens, num_q_heads, num_kv_heads, head_dim, positions,
+                                   positions_dtype, q_norm_weight, k_norm_weight, eps, rope_base, nullptr, stream);
 }
 
 int drafter_paged_attn(const void* qkv, int64_t qkv_row_stride, const void* k_pool, const void* v_pool,

@@ -55,6 +55,18 @@ def make_workspace(num_requests: int, tokens_per_block: int, num_q_heads: int, n
     return torch.zeros(n, dtype=torch.uint8, device=device)
 
 
+def _yarn(yarn: Optional[dict]):
+    """A YaRN parameter dict (``factor``, ``original_max_position``, optional ``alpha`` = 1 and
+    ``beta`` = 32) as the header's host struct, or None."""
+    if yarn is None:
+        return None
+    _check(isinstance(yarn, dict) and "factor" in yarn and "original_max_position" in yarn,
+           "yarn must be a dict with factor and original_max_position (alpha, beta optional)")
+    _check(set(yarn) <= {"factor", "original_max_position", "alpha", "beta"}, "unknown yarn parameter")
+    return ctypes.pointer(_lib.DaYarn(float(yarn["factor"]), int(yarn["original_max_position"]),
+                                      float(yarn.get("alpha", 1.0)), float(yarn.get("beta", 32.0))))
+
+
 def _check(cond: bool, msg: str):
     if not cond:
         raise DrafterAttnError(msg)
@@ -139,10 +151,14 @@ def drafter_attn_qknorm(qkv: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.T
                         k_norm_weight: torch.Tensor, *, num_q_heads: int, num_kv_heads: int,
                         tokens_per_block: int, block_lens: Optional[torch.Tensor] = None,
                         scale: Optional[float] = None, eps: float = 1e-5, rope_base: float = 10000.0,
-                        out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                        yarn: Optional[dict] = None, out: Optional[torch.Tensor] = None,
+                        workspace: Optional[torch.Tensor] = None,
                         status: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """k3_drafter_attn_qknorm (per-head q/k RMSNorm + NeoX RoPE in the kernel)."""
+    """k3_drafter_attn_qknorm (per-head q/k RMSNorm + NeoX RoPE in the kernel).  ``yarn``
+    (``factor``, ``original_max_position``, optional ``alpha``, ``beta``) selects YaRN-scaled
+    rotation (drafter_attn_qknorm_yarn)."""
     lib = _lib.load()
+    y = _yarn(yarn)
     a = _common(qkv, k_pool, v_pool, page_table, context_lens, block_lens, num_q_heads, num_kv_heads,
                 tokens_per_block, out, workspace)
     _check(positions.dtype in POS_DTYPES and positions.dim() == 1 and positions.numel() == a["R"] * a["T"]
@@ -154,27 +170,32 @@ def drafter_attn_qknorm(qkv: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.T
     if status is not None:
         _check(status.dtype == torch.int32 and status.numel() >= 1 and status.device == a["dev"],
                "status must be an int32 GPU tensor")
-    rc = lib.drafter_attn_qknorm(
-        qkv.data_ptr(), qkv.stride(0), k_pool.data_ptr(), v_pool.data_ptr(), k_pool.stride(0), k_pool.shape[0],
-        _ptr(page_table) if a["stride"] else None, a["stride"], context_lens.data_ptr(), _ptr(block_lens),
-        a["R"], a["T"], a["Hq"], a["Hkv"], HEAD_DIM, PAGE, scale,
-        positions.data_ptr(), POS_DTYPES[positions.dtype], q_norm_weight.data_ptr(), k_norm_weight.data_ptr(),
-        float(eps), float(rope_base),
-        a["workspace"].data_ptr(), a["workspace"].numel(), a["out"].data_ptr(), a["out"].stride(0),
-        _ptr(status), _stream(a["dev"]))
+    head = (qkv.data_ptr(), qkv.stride(0), k_pool.data_ptr(), v_pool.data_ptr(), k_pool.stride(0), k_pool.shape[0],
+            _ptr(page_table) if a["stride"] else None, a["stride"], context_lens.data_ptr(), _ptr(block_lens),
+            a["R"], a["T"], a["Hq"], a["Hkv"], HEAD_DIM, PAGE, scale,
+            positions.data_ptr(), POS_DTYPES[positions.dtype], q_norm_weight.data_ptr(), k_norm_weight.data_ptr(),
+            float(eps), float(rope_base))
+    tail = (a["workspace"].data_ptr(), a["workspace"].numel(), a["out"].data_ptr(), a["out"].stride(0),
+            _ptr(status), _stream(a["dev"]))
+    if y is None:
+        rc = lib.drafter_attn_qknorm(*head, *tail)
+    else:
+        rc = lib.drafter_attn_qknorm_yarn(*head, y, *tail)
     _raise(rc)
     return a["out"]
 
 
 def qk_norm_rope(qkv: torch.Tensor, positions: torch.Tensor, q_norm_weight: torch.Tensor,
                  k_norm_weight: torch.Tensor, *, num_q_heads: int, num_kv_heads: int, eps: float = 1e-5,
-                 rope_base: float = 10000.0) -> torch.Tensor:
+                 rope_base: float = 10000.0, yarn: Optional[dict] = None) -> torch.Tensor:
     """fused_qk_norm_rope (the drafter's cell), in place on ``qkv`` [N, >= (Hq+2Hkv)*64] bf16.
 
     Every q and k head of each row is RMS-normalised and NeoX-rotated at the row's
-    position; v heads and padding are left as they are.  Returns ``qkv``.
+    position; v heads and padding are left as they are.  Returns ``qkv``.  ``yarn``
+    as for ``drafter_attn_qknorm``.
     """
     lib = _lib.load()
+    y = _yarn(yarn)
     _check(qkv.device.type == "cuda", "qkv must be a GPU tensor (there is no CPU path)")
     _check(qkv.dtype == torch.bfloat16 and qkv.dim() == 2 and qkv.stride(1) == 1,
            "qkv must be bf16 [N, row_stride] with unit column stride")
@@ -186,9 +207,12 @@ def qk_norm_rope(qkv: torch.Tensor, positions: torch.Tensor, q_norm_weight: torc
     for name, wt in (("q_norm_weight", q_norm_weight), ("k_norm_weight", k_norm_weight)):
         _check(wt.dtype == torch.bfloat16 and tuple(wt.shape) == (HEAD_DIM,) and wt.is_contiguous()
                and wt.device == qkv.device, f"{name} must be bf16 [64]")
-    rc = lib.drafter_qk_norm_rope(qkv.data_ptr(), qkv.stride(0), N, Hq, Hkv, HEAD_DIM, positions.data_ptr(),
-                                  POS_DTYPES[positions.dtype], q_norm_weight.data_ptr(), k_norm_weight.data_ptr(),
-                                  float(eps), float(rope_base), _stream(qkv.device))
+    args = (qkv.data_ptr(), qkv.stride(0), N, Hq, Hkv, HEAD_DIM, positions.data_ptr(), POS_DTYPES[positions.dtype],
+            q_norm_weight.data_ptr(), k_norm_weight.data_ptr(), float(eps), float(rope_base))
+    if y is None:
+        rc = lib.drafter_qk_norm_rope(*args, _stream(qkv.device))
+    else:
+        rc = lib.drafter_qk_norm_rope_yarn(*args, y, _stream(qkv.device))
     _raise(rc)
     return qkv
 

@@ -21,6 +21,11 @@ int main(void) {
   rc = drafter_qk_norm_rope((void*)0x10000, 512, 0, 6, 1, 64, (const void*)0x900000, DA_POS_INT32,
                             (const void*)0x900100, (const void*)0x900200, 1e-5f, 10000.0f, NULL);
   if (rc != DA_EINVAL) { printf("rc %d\n", rc); return 1; }
+  /* YaRN parameters travel as a host struct; a factor below 1 is refused before any launch */
+  const da_yarn bad = {0.5f, 4096, 1.0f, 32.0f};
+  rc = drafter_qk_norm_rope_yarn((void*)0x10000, 512, 8, 6, 1, 64, (const void*)0x900000, DA_POS_INT32,
+                                 (const void*)0x900100, (const void*)0x900200, 1e-5f, 10000.0f, &bad, NULL);
+  if (rc != DA_EINVAL || strstr(drafter_attn_last_error(), "yarn") == NULL) { printf("yarn rc %d\n", rc); return 1; }
   printf("ok splits=%d pages=%d workspace=%zu flags=%d,%d,%d\n", splits, pages, ws, DA_FLAG_CONTEXT_LEN,
          DA_FLAG_PAGE_ID, DA_FLAG_BLOCK_LEN);
   return 0;

@@ -34,7 +34,8 @@ def _declared():
 def test_header_declares_entry_points():
     assert _declared() == sorted(["drafter_attn", "drafter_attn_qknorm", "drafter_attn_workspace_bytes",
                                   "drafter_attn_plan", "drafter_attn_last_error", "drafter_qk_norm_rope",
-                                  "drafter_kv_append", "drafter_paged_attn"])
+                                  "drafter_kv_append", "drafter_paged_attn", "drafter_attn_qknorm_yarn",
+                                  "drafter_qk_norm_rope_yarn"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -264,3 +265,35 @@ def test_small_arrays_must_be_aligned_to_their_elements(lib):
         assert "aligned" in _lib.last_error()
     assert _nr(lib, pos=0x900002) == DA_EINVAL and "aligned" in _lib.last_error()
     assert _nr(lib, pos=0x900004, pdt=1) == DA_EINVAL and "aligned" in _lib.last_error()
+
+
+@pytest.mark.parametrize("yarn", [
+    (0.5, 4096, 1.0, 32.0),              # factor below 1
+    (float("nan"), 4096, 1.0, 32.0),
+    (float("inf"), 4096, 1.0, 32.0),
+    (4.0, 0, 1.0, 32.0),                 # no original context
+    (4.0, 4096, 32.0, 32.0),             # empty ramp
+    (4.0, 4096, 5.0, 2.0),               # reversed ramp
+    (4.0, 4096, -1.0, 32.0),
+    (4.0, 4096, 1.0, float("nan")),
+])
+def test_yarn_parameters_rejected_before_launch(lib, yarn):
+    y = ctypes.pointer(_lib.DaYarn(*yarn))
+    rc = lib.drafter_qk_norm_rope_yarn(0x10000, 512, 8, 6, 1, 64, 0x900000, 0, 0x900100, 0x900200, 1e-5, 1e4, y, None)
+    assert rc == DA_EINVAL and "yarn" in _lib.last_error()
+    rc = lib.drafter_attn_qknorm_yarn(0x10000, 512, 0x200000, 0x202000, 16384, 4, 0x900000, 1, 0x900100, None,
+                                      1, 8, 6, 1, 64, 64, 0.125, 0x900200, 0, 0x900300, 0x900400, 1e-5, 1e4, y,
+                                      0xA00000, 1 << 20, 0xB00000, 384, None, None)
+    assert rc == DA_EINVAL and "yarn" in _lib.last_error()
+
+
+def test_binding_rejects_malformed_yarn():
+    from speculative_decoding_drafter_amd import DrafterAttnError
+    from speculative_decoding_drafter_amd.ops import _yarn
+
+    assert _yarn(None) is None
+    assert _yarn(dict(factor=4.0, original_max_position=4096)).contents.beta == 32.0
+    for bad in (dict(factor=4.0), dict(original_max_position=4096), (4.0, 4096),
+                dict(factor=4.0, original_max_position=4096, mscale=2.0)):
+        with pytest.raises(DrafterAttnError):
+            _yarn(bad)

@@ -38,7 +38,7 @@ def _paged_drop_last(qkv, k_pool, v_pool, page_table, kv_lens, block_lens=None, 
     return orig_paged(qkv, k_pool, v_pool, page_table, np.maximum(np.asarray(kv_lens) - 1, 0), block_lens, **kw)
 
 
-def _qknr_rotates_v(qkv, positions, qw, kw, *, num_q_heads, num_kv_heads, eps=1e-5, rope_base=1e4):
+def _qknr_rotates_v(qkv, positions, qw, kw, *, num_q_heads, num_kv_heads, eps=1e-5, rope_base=1e4, yarn=None):
     x = orig_qknr(qkv, positions, qw, kw, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads, eps=eps,
                   rope_base=rope_base)
     for g in range(num_kv_heads):
@@ -51,7 +51,7 @@ def _qknr_k_with_q_weight(qkv, positions, qw, kw, **kw2):
     return orig_qknr(qkv, positions, qw, qw, **kw2)
 
 
-def _qknr_rope_then_norm(qkv, positions, qw, kw, *, num_q_heads, num_kv_heads, eps=1e-5, rope_base=1e4):
+def _qknr_rope_then_norm(qkv, positions, qw, kw, *, num_q_heads, num_kv_heads, eps=1e-5, rope_base=1e4, yarn=None):
     x = np.array(qkv, dtype=np.float64, copy=True)
     pos = np.asarray(positions)
     for h in range(num_q_heads):
@@ -63,7 +63,7 @@ def _qknr_rope_then_norm(qkv, positions, qw, kw, *, num_q_heads, num_kv_heads, e
     return x
 
 
-def _qknr_skip_last_k(qkv, positions, qw, kw, *, num_q_heads, num_kv_heads, eps=1e-5, rope_base=1e4):
+def _qknr_skip_last_k(qkv, positions, qw, kw, *, num_q_heads, num_kv_heads, eps=1e-5, rope_base=1e4, yarn=None):
     x = orig_qknr(qkv, positions, qw, kw, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads, eps=eps,
                   rope_base=rope_base)
     c = mod.k_cols(num_kv_heads - 1, num_q_heads, num_kv_heads)
@@ -71,7 +71,9 @@ def _qknr_skip_last_k(qkv, positions, qw, kw, *, num_q_heads, num_kv_heads, eps=
     return x
 
 
-def _rope_sign(x, pos, base):
+def _rope_sign(x, pos, base, yarn=None):
+    if yarn is not None:
+        return orig_rope(x, pos, base, yarn)
     x = np.asarray(x, dtype=np.float64)
     ang = np.asarray(pos, dtype=np.float64)[..., None] * orig_freq(base, x.shape[-1])
     c, s = np.cos(ang), np.sin(ang)
@@ -79,7 +81,9 @@ def _rope_sign(x, pos, base):
     return np.concatenate([x1 * c + x2 * s, x2 * c - x1 * s], axis=-1)
 
 
-def _rope_interleaved(x, pos, base):
+def _rope_interleaved(x, pos, base, yarn=None):
+    if yarn is not None:
+        return orig_rope(x, pos, base, yarn)
     x = np.asarray(x, dtype=np.float64)
     ang = np.asarray(pos, dtype=np.float64)[..., None] * orig_freq(base, x.shape[-1])
     c, s = np.cos(ang), np.sin(ang)
@@ -88,6 +92,24 @@ def _rope_interleaved(x, pos, base):
     y[..., 0::2] = x1 * c - x2 * s
     y[..., 1::2] = x2 * c + x1 * s
     return y
+
+
+orig_yfreq = mod.yarn_inv_freq
+orig_mscale = mod.yarn_mscale
+
+
+def _yarn_ramp_reversed(base, factor, L, alpha=1.0, beta=32.0, dim=64):
+    theta = orig_freq(base, dim)
+    g = np.clip((beta - L * theta / (2 * np.pi)) / (beta - alpha), 0.0, 1.0)
+    return (1 - g) * theta / factor + g * theta
+
+
+def _yarn_turns_without_2pi(base, factor, L, alpha=1.0, beta=32.0, dim=64):
+    return orig_yfreq(base, factor, L * 2 * np.pi, alpha, beta, dim)
+
+
+def _yarn_times_s(base, factor, L, alpha=1.0, beta=32.0, dim=64):
+    return orig_yfreq(base, 1.0 / factor, L, alpha, beta, dim)
 
 
 def _gather_shift_slot(k_pool, v_pool, row, L, g):
@@ -136,7 +158,7 @@ MUTATIONS = {
     "rms_no_weight": ("rms_norm", lambda x, w, eps: orig_rms(x, np.ones_like(w), eps)),
     "rope_sign": ("rope_neox", _rope_sign),
     "rope_interleaved": ("rope_neox", _rope_interleaved),
-    "rope_pos_plus_one": ("rope_neox", lambda x, pos, base: orig_rope(x, np.asarray(pos) + 1, base)),
+    "rope_pos_plus_one": ("rope_neox", lambda x, pos, base, yarn=None: orig_rope(x, np.asarray(pos) + 1, base, yarn)),
     "rope_exponent": ("rope_inv_freq", lambda base, dim=64: np.power(float(base), -np.arange(dim // 2) / dim)),
     "rope_base_1000": ("rope_inv_freq", lambda base, dim=64: orig_freq(1000.0, dim)),
     "gather_slot_shift": ("gather_context", _gather_shift_slot),
@@ -158,6 +180,11 @@ MUTATIONS = {
     "append_next_slot": ("kv_append", _append_next_slot),
     "append_v_as_k": ("kv_append", _append_v_as_k),
     "paged_drops_last_key": ("paged_attn", _paged_drop_last),
+    "yarn_ramp_reversed": ("yarn_inv_freq", _yarn_ramp_reversed),
+    "yarn_turns_without_2pi": ("yarn_inv_freq", _yarn_turns_without_2pi),
+    "yarn_multiplies_by_s": ("yarn_inv_freq", _yarn_times_s),
+    "yarn_mscale_log10": ("yarn_mscale", lambda f: 0.1 * np.log10(f) + 1.0),
+    "yarn_no_mscale": ("yarn_mscale", lambda f: 1.0),
 }
 
 
@@ -177,7 +204,9 @@ def _battery():
         except Exception:  # any error is a failed pin
             failed.append(f"bruteforce{i}")
     for name in ("test_rmsnorm_closed_forms", "test_rope_closed_forms", "test_qk_norm_rope_closed_forms",
-                 "test_qk_norm_rope_constant_heads_at_position_zero"):
+                 "test_qk_norm_rope_constant_heads_at_position_zero", "test_yarn_factor_one_is_plain_rope",
+                 "test_yarn_short_original_context_is_position_interpolation",
+                 "test_yarn_long_original_context_only_scales", "test_yarn_ramp_midpoint_and_shape"):
         try:
             getattr(pins, name)()
         except Exception:  # any error is a failed pin

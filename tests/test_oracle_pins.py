@@ -257,6 +257,72 @@ def test_rope_closed_forms():
     np.testing.assert_allclose(np.hypot(y[:, :32], y[:, 32:]), np.hypot(x[:, :32], x[:, 32:]), rtol=1e-13)
 
 
+# ---- YaRN ("YaRN 4.0" of the drafter checkpoint; the method as published).  The pins use
+# special cases with closed forms: factor 1 is plain RoPE; an original context so short that no
+# pair turns once is position interpolation (every frequency / s); one so long that every pair
+# turns more than beta times keeps every frequency; factors e and e^10 give the temperature
+# factors 1.1 and 2.0 exactly; and a chosen context puts one pair at the middle of the ramp.
+
+def _xp():
+    rng = np.random.default_rng(21)
+    return rng.standard_normal((6, 64)), np.array([0, 4, 8, 401, 2044, 40000])
+
+
+def test_yarn_factor_one_is_plain_rope():
+    x, pos = _xp()
+    for L in (1, 64, 4096, 10 ** 9):
+        a = oracle.rope_neox(x, pos, 1e4, dict(factor=1.0, original_max_position=L))
+        # (1 - g) * f + g * f rounds within an ulp of f: angles near 4e4 agree to ~1e-11
+        np.testing.assert_allclose(a, oracle.rope_neox(x, pos, 1e4), rtol=0, atol=1e-10)
+
+
+def test_yarn_short_original_context_is_position_interpolation():
+    x, pos = _xp()
+    a = oracle.rope_neox(x, pos, 1e4, dict(factor=math.e, original_max_position=1))
+    np.testing.assert_allclose(a, 1.1 * oracle.rope_neox(x, pos / math.e, 1e4), rtol=0, atol=1e-9)
+
+
+def test_yarn_long_original_context_only_scales():
+    x, pos = _xp()
+    a = oracle.rope_neox(x, pos, 1e4, dict(factor=math.e ** 10, original_max_position=10 ** 12))
+    np.testing.assert_allclose(a, 2.0 * oracle.rope_neox(x, pos, 1e4), rtol=0, atol=1e-9)
+
+
+def test_yarn_ramp_midpoint_and_shape():
+    i = np.arange(32)
+    theta = 10.0 ** (-i / 8.0)                      # 10000**(-2i/64)
+    # pair 8 (frequency 0.1) turns 16.5 times over L = 16.5 * 2 pi / 0.1: half way from 1 to 32
+    f = oracle.yarn_inv_freq(1e4, 4.0, 16.5 * 2 * math.pi / 0.1, 1.0, 32.0)
+    ratio = f / theta
+    assert abs(ratio[8] - (0.5 / 4 + 0.5)) < 1e-12
+    assert ratio[0] == 1.0 and abs(ratio[31] - 0.25) < 1e-15
+    assert np.all(np.diff(ratio) <= 1e-15) and np.all((ratio >= 0.25 - 1e-15) & (ratio <= 1.0))
+    # at the drafter's factor over a 4096-token original context all three regimes occur
+    r4 = oracle.yarn_inv_freq(1e4, 4.0, 4096) / theta
+    assert (r4 == 1.0).any() and (np.abs(r4 - 0.25) < 1e-15).any() and ((r4 > 0.26) & (r4 < 0.99)).any()
+
+
+def test_yarn_attention_equals_explicit_steps():
+    # the qknorm attention with YaRN == plain attention on q/k normalised and YaRN-rotated first
+    yarn = dict(factor=4.0, original_max_position=256)
+    case = ds.make_case(3, 5, 12, 2, [100, 0, 700], seed=22, qknorm=True, pos_dtype=torch.int64,
+                        pos_offset=[5000, 0, 30000])
+    a = case.np_args()
+    fused = oracle.drafter_attn_qknorm(**a, yarn=yarn)
+    q = a["qkv"].copy()
+    for h in range(case.Hq):
+        c = slice(h * 64, (h + 1) * 64)
+        q[:, c] = oracle.rope_neox(oracle.rms_norm(q[:, c], a["q_norm_weight"], 1e-5), a["positions"], 1e4, yarn)
+    for g in range(case.Hkv):
+        c = slice((case.Hq + g) * 64, (case.Hq + g + 1) * 64)
+        q[:, c] = oracle.rope_neox(oracle.rms_norm(q[:, c], a["k_norm_weight"], 1e-5), a["positions"], 1e4, yarn)
+    b = dict(a)
+    b["qkv"] = q
+    np.testing.assert_allclose(oracle.drafter_attn(**b), fused, rtol=0, atol=1e-12)
+    # and the temperature is really applied: without YaRN the result differs
+    assert np.abs(oracle.drafter_attn_qknorm(**a) - fused).max() > 1e-3
+
+
 def test_rope_relative_position_property():
     # with no context, scores depend only on position differences: shift all positions
     case = ds.make_case(2, 6, 12, 2, [0, 0], seed=8, stride=0, qknorm=True)
