@@ -99,7 +99,7 @@ enum {
  * Bytes of workspace a call with these sizes needs (0 for arguments outside the
  * contract).  The workspace holds one fp32 partial (running max, weight sum,
  * unnormalised output) per (request, KV head, context split) and one counter
- * per (request, KV head).  The workspace must be 256-byte aligned (as hipMalloc
+ * per (request, KV head), each counter on its own 256-byte line.  The workspace must be 256-byte aligned (as hipMalloc
  * returns).  The counters must be zero before the first call on a workspace
  * (zero the whole buffer once after allocating it); every call leaves them zero
  * again.  Two calls in flight on one workspace race.

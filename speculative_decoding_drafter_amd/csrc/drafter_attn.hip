@@ -53,6 +53,9 @@ constexpr int kMaxPagesPerSplit = 64 * kWaves;  // a wave's page ids fit one 64-
 constexpr int kTileBytes = kPage * kD * 2;   // one [64][64] bf16 tile, 8 KiB
 constexpr int kStageBytes = 2 * kTileBytes;  // a wave's K slot then V slot
 constexpr float kRescaleLog2 = 8.0f;         // lazy-rescale headroom (exp2 units)
+// Arrival counters sit 256 bytes apart: the 8 or so workgroups of every (r, g) bump
+// theirs at about the same time, and atomics to one line queue behind each other.
+constexpr int kCounterStride = 64;           // uint32 units
 
 // LDS layout (bytes)
 constexpr int kOffQ = 0;                                   // [48][64] bf16 query tile
@@ -107,7 +110,7 @@ struct Params {
   const uint16_t* wk;
   float* part_o;     // [R*Hkv*S][48][64]
   float* part_ml;    // [R*Hkv*S][48][2]
-  uint32_t* counters;  // [R*Hkv]
+  uint32_t* counters;  // [R*Hkv][kCounterStride], word 0 of each used
   uint16_t* out;
   int64_t out_stride;
   int32_t* status;
@@ -786,9 +789,10 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
   __syncthreads();
   int* last = reinterpret_cast<int*>(smem + kOffFlag);
   if (tid == 0) {
-    const uint32_t prev = __hip_atomic_fetch_add(p.counters + rg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t* ctr = p.counters + kCounterStride * rg;
+    const uint32_t prev = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const int is_last = (prev == static_cast<uint32_t>(s_used - 1));
-    if (is_last) __hip_atomic_store(p.counters + rg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (is_last) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     *last = is_last;
   }
   __syncthreads();
@@ -985,7 +989,7 @@ struct WsLayout {
 WsLayout ws_layout(int R, int Hkv, int S) {
   WsLayout l;
   l.counters = 0;
-  l.part_o = align256(static_cast<size_t>(R) * Hkv * 4);
+  l.part_o = align256(static_cast<size_t>(R) * Hkv * kCounterStride * 4);
   l.part_ml = l.part_o + align256(static_cast<size_t>(R) * Hkv * S * kRows * kD * 4);
   l.total = l.part_ml + align256(static_cast<size_t>(R) * Hkv * S * kRows * 2 * 4);
   return l;

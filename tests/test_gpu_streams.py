@@ -16,8 +16,9 @@ pytestmark = pytest.mark.gpu
 
 
 def _counters(ws: torch.Tensor, R: int, Hkv: int) -> torch.Tensor:
-    # the workspace starts with one 32-bit arrival counter per (request, KV head)
-    return ws[:4 * R * Hkv].view(torch.int32)
+    # the workspace starts with one 32-bit arrival counter per (request, KV head), 256 bytes apart
+    # (the words between them are never touched: the whole region must read zero)
+    return ws[:256 * R * Hkv].view(torch.int32)
 
 
 @pytest.mark.parametrize("name", ["cfg2", "cfg3", "short_and_long", "single_split"])
