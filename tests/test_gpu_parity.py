@@ -240,6 +240,31 @@ def test_pages_beyond_2_31_elements_of_pool():
     check(to_np(out), reference(case), "pool-beyond-2^31")
 
 
+@pytest.mark.parametrize("scale", [2.0, 4.0, 1e-4])
+def test_sharp_and_flat_softmax(scale):
+    # scale 2-4 (16-32x the usual): the softmax is close to one-hot and the running maximum
+    # jumps by more than the lazy-rescale headroom page after page; 1e-4: nearly uniform.
+    # Plain path only: q and k are exact bf16 inputs there.  (With qknorm the bf16 rounding of
+    # the normalised q/k that the contractions need moves a near one-hot softmax by more than
+    # the bar at such scales -- 773 elements out at scale 4, 28 at scale 1, in fp64 alone.)
+    case = ds.make_case(3, 8, 24, 4, [2041, 700, 5000], seed=97, scale=scale)
+    say(f"softmax scale {scale}")
+    check(to_np(run(case)), reference(case), f"scale{scale}")
+
+
+def test_rising_scores_force_rescales():
+    # keys grow along the context (x1 .. x16), so page after page holds a larger maximum: every
+    # wave's reference maximum moves many times (the rescale path), against fp64
+    case = ds.make_case(2, 8, 12, 2, [4096, 1500], seed=98, scale=0.5)
+    ramp = torch.ones(case.k_pool.shape[0], 1, 1, 1)
+    for r, L in enumerate(case.context_lens.tolist()):
+        for j in range(-(-L // 64)):
+            ramp[int(case.page_table[r, j])] = 1.0 + 15.0 * j / max(1, -(-L // 64) - 1)
+    case.k_pool.copy_((case.k_pool.float() * ramp).to(torch.bfloat16))   # a view into the fused pool
+    say("rising scores")
+    check(to_np(run(case)), reference(case), "rising")
+
+
 def test_status_flags_and_clamping():
     # device-value contract breaks are clamped (no out-of-range reads) and reported
     case = ds.make_case(2, 2, 6, 1, [100, 50], seed=5, stride=2, pool_pages=4)
