@@ -4,14 +4,16 @@ Each case draws R, T in 1..8, Hkv in {1, 2, 4, 8, 16}, context lengths biased
 toward page edges (0, 64k-1, 64k, 64k+1) up to 4 pages past a few hundred,
 a page-table stride at or above the need, ragged block lengths, qknorm or
 plain, int32 or int64 positions with offsets, poison, qkv row padding and
-separate pools.  Each must meet the acceptance bar; a rerun must be
-bit-identical.  Also: the binding refuses wrong dtypes and shapes.
+separate pools; about a third of the qknorm cases use YaRN with drawn
+parameters.  Each must meet the acceptance bar; a rerun must be bit-identical.
+Also: the binding refuses wrong dtypes and shapes.
 """
 import numpy as np
 import pytest
 import torch
 
 import drafter_synth as ds
+import oracle
 from tests.gpu_util import check, reference, run, say, to_np
 
 pytestmark = pytest.mark.gpu
@@ -39,17 +41,31 @@ def _draw(i: int) -> ds.DrafterCase:
         pos_offset=[int(x) for x in rng.integers(0, 100000, R)] if qknorm and rng.random() < 0.5 else None)
 
 
+def _yarn_draw(i: int, case: ds.DrafterCase):
+    # about a third of the qknorm cases use YaRN with drawn parameters
+    rng = np.random.default_rng(9500 + i)
+    if not case.qknorm or rng.random() >= 0.35:
+        return None
+    a = float(rng.uniform(0.0, 4.0))
+    return dict(factor=float(rng.choice([1.0, 2.0, 4.0, 8.0])), original_max_position=int(rng.choice([256, 4096, 32768])),
+                alpha=a, beta=a + float(rng.uniform(1.0, 64.0)))
+
+
 @pytest.mark.parametrize("i", range(40))
 def test_random_case(i):
     case = _draw(i)
+    yarn = _yarn_draw(i, case)
     say(f"random {i}: R={case.R} T={case.T} Hkv={case.Hkv} lens={case.context_lens.tolist()} "
-        f"stride={case.stride} qknorm={case.qknorm} blens={None if case.block_lens is None else case.block_lens.tolist()}")
+        f"stride={case.stride} qknorm={case.qknorm} blens={None if case.block_lens is None else case.block_lens.tolist()} "
+        f"yarn={yarn}")
     g = ds.to_device(case, "cuda")
-    out = run(case, g)
-    again = run(case, g)
+    kw = {} if yarn is None else dict(yarn=yarn)
+    out = run(case, g, **kw)
+    again = run(case, g, **kw)
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), again.view(torch.int16)), "rerun not bit-identical"
-    check(to_np(out), reference(case), f"random{i}")
+    ref = reference(case) if yarn is None else oracle.drafter_attn_qknorm(**case.np_args(), yarn=yarn)
+    check(to_np(out), ref, f"random{i}")
 
 
 def test_binding_refuses_wrong_dtypes_and_shapes():
