@@ -217,6 +217,19 @@ def make_case(R: int, T: int, Hq: int, Hkv: int, lens: Sequence[int], *,
         scale=1.0 / math.sqrt(D) if scale is None else scale, qknorm=qknorm, name=name)
 
 
+def device_normal_pool(pages: int, Hkv: int, *, seed: int, device, chunk_pages: int = 2048) -> torch.Tensor:
+    """A ``[pages, 2, Hkv, 64, 64]`` bf16 pool ~ N(0,1) drawn on ``device`` with torch's seeded
+    counter-based generator, a chunk of pages at a time -- for pools too large to draw on the
+    host in reasonable time (pass it to ``make_case(pool_override=...)``)."""
+    gen = torch.Generator(device=device).manual_seed(seed)
+    pool = torch.empty((pages, 2, Hkv, PAGE, HEAD_DIM), dtype=torch.bfloat16, device=device)
+    for p0 in range(0, pages, chunk_pages):
+        p1 = min(pages, p0 + chunk_pages)
+        pool[p0:p1] = torch.randn((p1 - p0, 2, Hkv, PAGE, HEAD_DIM), generator=gen, device=device,
+                                  dtype=torch.float32).to(torch.bfloat16)
+    return pool
+
+
 # --------------------------------------------------------------------------------------
 # The five benchmark-style workloads
 # --------------------------------------------------------------------------------------

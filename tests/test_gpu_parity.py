@@ -216,6 +216,31 @@ def test_widest_head_layout_long_contexts():
     check(to_np(run(case)), reference(case), "h96x16")
 
 
+def test_widest_layout_at_the_longest_row():
+    # 96/16 heads with a 1,048,576-token context: the largest pages per split (512, 64 per
+    # wave), 32 splits x 16 KV heads = 512 workgroups (two per CU in turn) and 512 partial
+    # slots.  The 4.3 GB pool is drawn on the device; KV groups 0, 7 and 15 (their 6 query
+    # heads each) are checked against fp64 one by one.
+    pages = 16384
+    pool = ds.device_normal_pool(pages + 3, 16, seed=99, device="cuda")
+    case = ds.make_case(1, 8, 96, 16, [pages * 64], seed=99, stride=pages, pool_pages=pages + 3, qknorm=True,
+                        pos_dtype=torch.int64, pool_override=pool)
+    g = ds.to_device(case, "cuda")
+    say("96/16 heads, 1M-token context")
+    out = to_np(run(case, g))
+    pt = case.page_table.numpy().astype(np.int64)
+    cl = case.context_lens.numpy().astype(np.int64)
+    for grp in (0, 7, 15):
+        cols = (list(range(6 * grp * 64, 6 * (grp + 1) * 64)) + list(range((96 + grp) * 64, (97 + grp) * 64)) +
+                list(range((112 + grp) * 64, (113 + grp) * 64)))
+        ref = oracle.drafter_attn_qknorm(
+            case.qkv[:, cols].double().numpy(), g.k_pool[:, grp:grp + 1].double().cpu().numpy(),
+            g.v_pool[:, grp:grp + 1].double().cpu().numpy(), pt, cl, positions=case.positions.numpy(),
+            q_norm_weight=case.q_norm_weight.double().numpy(), k_norm_weight=case.k_norm_weight.double().numpy(),
+            num_q_heads=6, num_kv_heads=1, tokens_per_block=8, scale=case.scale)
+        check(out[:, 6 * grp * 64:6 * (grp + 1) * 64], ref, f"h96x16-1M-group{grp}")
+
+
 def test_pages_beyond_2_31_elements_of_pool():
     # with 96/16 heads a page is 128 KiB per pool: ids near 40,000 put a page 5.2 GB (2.6e9
     # elements) into each pool, past any 32-bit element or byte offset; every other page is NaN
