@@ -241,6 +241,32 @@ def test_widest_layout_at_the_longest_row():
         check(out[:, 6 * grp * 64:6 * (grp + 1) * 64], ref, f"h96x16-1M-group{grp}")
 
 
+def test_every_dimension_at_its_maximum():
+    # 8 requests x 8 tokens x 96/16 heads, every context 1,048,576 tokens: 4096 workgroups (16 per
+    # CU in turn), a 34 GB pool drawn on the device.  Sampled (request, KV group) pairs are checked
+    # against fp64 one by one, each on its own request's pages gathered into a small pool.
+    pages = 16384
+    pool = ds.device_normal_pool(8 * pages, 16, seed=100, device="cuda")
+    case = ds.make_case(8, 8, 96, 16, [pages * 64] * 8, seed=100, stride=pages, pool_pages=8 * pages, qknorm=True,
+                        pos_dtype=torch.int64, pool_override=pool)
+    g = ds.to_device(case, "cuda")
+    say("8 x 8 x 96/16, 1M-token contexts")
+    out = to_np(run(case, g))
+    for r, grp in ((0, 0), (3, 9), (7, 15)):
+        rows = slice(8 * r, 8 * (r + 1))
+        cols = (list(range(6 * grp * 64, 6 * (grp + 1) * 64)) + list(range((96 + grp) * 64, (97 + grp) * 64)) +
+                list(range((112 + grp) * 64, (113 + grp) * 64)))
+        ids = g.page_table[r].long()
+        kp = g.k_pool[ids, grp:grp + 1].double().cpu().numpy()
+        vp = g.v_pool[ids, grp:grp + 1].double().cpu().numpy()
+        ref = oracle.drafter_attn_qknorm(
+            case.qkv[rows][:, cols].double().numpy(), kp, vp, np.arange(pages, dtype=np.int64)[None, :],
+            np.array([pages * 64]), positions=case.positions[rows].numpy(),
+            q_norm_weight=case.q_norm_weight.double().numpy(), k_norm_weight=case.k_norm_weight.double().numpy(),
+            num_q_heads=6, num_kv_heads=1, tokens_per_block=8, scale=case.scale)
+        check(out[rows, 6 * grp * 64:6 * (grp + 1) * 64], ref, f"max-all-r{r}-group{grp}")
+
+
 def test_pages_beyond_2_31_elements_of_pool():
     # with 96/16 heads a page is 128 KiB per pool: ids near 40,000 put a page 5.2 GB (2.6e9
     # elements) into each pool, past any 32-bit element or byte offset; every other page is NaN
