@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--yarn", action="store_true",
                     help="YaRN-scaled rotation (factor 4, 4096-token original context, ramp 1..32) in the qknorm "
                          "call; reported beside the headline, not instead of it")
+    ap.add_argument("--large", action="store_true",
+                    help="instead of the headline line: one line per large context (131k and 1M tokens, "
+                         "24/4 and 96/16 heads), pools drawn on the device")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=10.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -187,6 +190,52 @@ def write_traffic(fetch_csv: str, write_csv: str, workload: int, dest: str = Non
     return rec
 
 
+LARGE = [(8, 24, 4, 2048), (8, 24, 4, 16384), (8, 96, 16, 16384)]  # R, Hq, Hkv, pages per request
+
+
+def large_contexts(args):
+    """Context lengths beyond the headline workload (8 x 8 tokens, qknorm, every request at the
+    same length): 131k tokens at 24/4 heads, 1M tokens at 24/4 and at 96/16 heads.  The pools
+    (1.1 to 34 GB, all larger than the 256 MB Infinity Cache) are drawn on the device; one JSON
+    line per size, mean of event-timed calls after warm-up."""
+    import torch
+
+    import drafter_synth as ds
+    from speculative_decoding_drafter_amd import drafter_attn_qknorm, make_workspace
+
+    for R, Hq, Hkv, pages in LARGE:
+        pool = ds.device_normal_pool(R * pages, Hkv, seed=5, device="cuda")
+        case = ds.make_case(R, 8, Hq, Hkv, [pages * 64] * R, seed=5, stride=pages, pool_pages=R * pages,
+                            qknorm=True, pool_override=pool)
+        g = ds.to_device(case, "cuda")
+        ws = make_workspace(R, 8, Hq, Hkv, pages, "cuda")
+        out = torch.empty(R * 8, Hq * 64, dtype=torch.bfloat16, device="cuda")
+
+        def call():
+            drafter_attn_qknorm(g.qkv, g.k_pool, g.v_pool, g.page_table, g.context_lens, g.positions,
+                                g.q_norm_weight, g.k_norm_weight, num_q_heads=Hq, num_kv_heads=Hkv,
+                                tokens_per_block=8, out=out, workspace=ws)
+        for _ in range(args.warmup // 4 + 1):
+            call()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(max(5, args.steps // 20))]
+        for a, b in evs:
+            a.record()
+            call()
+            b.record()
+        torch.cuda.synchronize()
+        ms = sum(a.elapsed_time(b) for a, b in evs) / len(evs)
+        kv = R * pages * Hkv * 2 * 64 * 64 * 2
+        print(json.dumps({"metric": "K/V-read HBM GB/s at large contexts", "requests": R, "tokens": 8,
+                          "q_heads": Hq, "kv_heads": Hkv, "context_tokens": pages * 64, "kv_bytes_per_call": kv,
+                          "us_per_call": round(ms * 1e3, 1), "GBs": round(kv / (ms * 1e-3) / 1e9, 1),
+                          "pct_of_hbm_peak": round(100 * kv / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 1),
+                          "calls_timed": len(evs)}), flush=True)
+        del pool, case, g, ws, out
+        torch.cuda.empty_cache()
+
+
 def ab_replaced(args):
     """Fused op vs the path it replaces on the same workload (one fresh pool page per request
     for the appended slots).  Each step is timed alone after the cache flush; the two are
@@ -290,6 +339,9 @@ def main():
         sys.exit(2)
     if args.ab_replaced:
         ab_replaced(args)
+        return
+    if args.large:
+        large_contexts(args)
         return
     import torch
 
