@@ -4,16 +4,17 @@ Default workload: 8 requests x 8 draft tokens, 24 query / 4 KV heads, head_dim 6
 context 32768 tokens per request (512 HND pages of 64 each, 4096 pages shuffled
 across a 5000-page bf16 pool), per-head q/k RMSNorm + NeoX RoPE in the kernel.
 
-A step is one call of drafter_attn_qknorm (one kernel launch; ``--graph`` captures
-it once in a HIP graph and replays that instead).  Inputs are resident in HBM
-before timing starts.  Before every step (warm-up and timed)
-an untimed kernel reads a 1 GiB buffer so that neither the L2 nor the 256 MB
-Infinity Cache holds the 268 MB of K/V the call reads: each timed call streams
-its pages from HBM.  (The flush only reads, so it leaves no dirty lines whose
-write-back would compete with the timed call.)  Each call is bracketed by HIP events on the
+A step is one call of drafter_attn_qknorm (one kernel launch).  The same run also
+captures one call in a HIP graph and times its replays the same way
+(``graph_us_per_call``); ``--graph`` makes the replays the headline instead.
+Inputs are resident in HBM before timing starts.  Before every step (warm-up and
+timed) an untimed kernel reads a 1 GiB buffer so that neither the L2 nor the 256 MB
+Infinity Cache holds the 268 MB of K/V the call reads: each timed call streams its
+pages from HBM.  (The flush only reads, so it leaves no dirty lines whose write-back
+would compete with the timed call.)  Each call is bracketed by HIP events on the
 stream it is launched on; ms_per_step is their mean (the median and p10/p90 are
-reported too).  ``--hot`` times
-back-to-back calls without the flush instead (reported, not the headline).
+reported too).  ``--hot`` times back-to-back calls without the flush instead
+(reported, not the headline).
 
 value = algorithmic K/V bytes per call / mean call time (GB/s): every context
 K and V element is read exactly once, sum_r L_r * Hkv * 64 * 2 * 2 bytes.
@@ -38,9 +39,8 @@ def parse():
     ap.add_argument("--config", type=int, default=5, choices=[1, 2, 3, 5])
     ap.add_argument("--hot", action="store_true", help="no cache flush between calls")
     ap.add_argument("--graph", action="store_true",
-                    help="replay one call captured in a HIP graph instead of launching it directly "
-                         "(measured +7.2 us per call between the events with the runtime's default graph "
-                         "packet capture, +3.8 us with DEBUG_CLR_GRAPH_PACKET_CAPTURE=0 in the environment)")
+                    help="headline from replays of one call captured in a HIP graph instead of direct launches "
+                         "(every run times both modes and reports the other beside the headline)")
     ap.add_argument("--yarn", action="store_true",
                     help="YaRN-scaled rotation (factor 4, 4096-token original context, ramp 1..32) in the qknorm "
                          "call; reported beside the headline, not instead of it")
@@ -109,7 +109,8 @@ def cpu_baseline(case, budget_s: float):
     except Exception:  # pragma: no cover
         threads, threadpool_limits = 1, None
     gbs, n_req, dt = _oracle_rate(case, budget_s)
-    out = {"value": round(gbs, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+    out = {"value": round(gbs, 4), "unit": "GB/s", "cores": int(threads), "host_cores": os.cpu_count(),
+           "kind": "oracle",
            "sample": f"{n_req} request-passes over the {case.R} requests of the same workload "
                      f"(fp64 numpy oracle, {n_req / case.R:.2f} calls' worth), {dt:.1f} s"}
     if threadpool_limits is not None:
@@ -368,40 +369,46 @@ def main():
     flush = None if args.hot else torch.ones(1 << 28, dtype=torch.float32, device=dev)
     flush_out = torch.empty((), dtype=torch.float32, device=dev)
 
-    step = call
-    if args.graph:
-        # one call captured in a HIP graph (after an eager warm-up); each step replays it
+    # one call captured in a HIP graph (after an eager warm-up); replaying it is the other launch mode
+    call()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
         call()
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            call()
-        torch.cuda.synchronize()
-        step = graph.replay
+    torch.cuda.synchronize()
+    headline, other = (graph.replay, call) if args.graph else (call, graph.replay)
 
-    def one(timed_events=None):
-        if flush is not None:
-            torch.sum(flush, dim=0, out=flush_out)
-        if timed_events is None:
-            step()
-        else:
-            timed_events[0].record()
-            step()
-            timed_events[1].record()
+    def timed(step):
+        """Warm-up, then each of args.steps calls alone between HIP events (after the flush):
+        (sorted times in ms, wall seconds of the timed region)."""
+        def one(timed_events=None):
+            if flush is not None:
+                torch.sum(flush, dim=0, out=flush_out)
+            if timed_events is None:
+                step()
+            else:
+                timed_events[0].record()
+                step()
+                timed_events[1].record()
 
-    for _ in range(args.warmup):
-        one()
-    torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for e in evs:
-        one(e)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    times_ms = sorted(a.elapsed_time(b) for a, b in evs)
+        for _ in range(args.warmup):
+            one()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        t0 = time.perf_counter()
+        for e in evs:
+            one(e)
+        torch.cuda.synchronize()
+        return sorted(a.elapsed_time(b) for a, b in evs), time.perf_counter() - t0
+
+    pct = lambda ts: [round(ts[int(q * (len(ts) - 1))] * 1e3, 3) for q in (0.1, 0.5, 0.9)]
+    times_ms, wall = timed(headline)
     mean_ms = sum(times_ms) / len(times_ms)
     p10, p50, p90 = (times_ms[int(q * (len(times_ms) - 1))] for q in (0.1, 0.5, 0.9))
+    # the other launch mode on the same buffers, timed the same way (reported beside the headline)
+    other_ms, _ = timed(other)
+    other_mean = sum(other_ms) / len(other_ms)
 
     if args.calibrate_copy:
         src = torch.empty(1 << 29, dtype=torch.uint8, device=dev).fill_(1)
@@ -436,6 +443,9 @@ def main():
         "rope": "yarn factor 4, original context 4096, ramp 1..32" if yarn else "neox",
         "launch": ("HIP graph replay (DEBUG_CLR_GRAPH_PACKET_CAPTURE=%s)"
                    % os.environ.get("DEBUG_CLR_GRAPH_PACKET_CAPTURE", "unset")) if args.graph else "direct",
+        ("direct_us_per_call" if args.graph else "graph_us_per_call"): round(other_mean * 1e3, 3),
+        ("direct_us_p10_p50_p90" if args.graph else "graph_us_p10_p50_p90"): pct(other_ms),
+        "graph_packet_capture_env": os.environ.get("DEBUG_CLR_GRAPH_PACKET_CAPTURE", "unset"),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -324,6 +324,30 @@ def with_append_room(case: DrafterCase, seed: int) -> DrafterCase:
     return dataclasses.replace(case, pool=pool, k_pool=pool[:, 0], v_pool=pool[:, 1], page_table=table)
 
 
+def splice_request(base: DrafterCase, donor: DrafterCase, k: int) -> DrafterCase:
+    """``base`` with request ``k``'s inputs taken from ``donor``: its qkv rows, page-table row,
+    context length, positions and block length.  Both cases must have the same sizes and
+    share one pool (e.g. split-sweep cells drawn over ``config4_pool``)."""
+    assert (base.R, base.T, base.Hq, base.Hkv, base.stride) == (donor.R, donor.T, donor.Hq, donor.Hkv, donor.stride)
+    T = base.T
+    rows = slice(k * T, (k + 1) * T)
+    out = dataclasses.replace(base)
+    out.qkv = base.qkv.clone()
+    out.qkv[rows] = donor.qkv[rows]
+    out.page_table = base.page_table.clone()
+    out.page_table[k] = donor.page_table[k]
+    out.context_lens = base.context_lens.clone()
+    out.context_lens[k] = donor.context_lens[k]
+    if base.positions is not None:
+        out.positions = base.positions.clone()
+        out.positions[rows] = donor.positions[rows]
+    if base.block_lens is not None:
+        out.block_lens = base.block_lens.clone()
+        out.block_lens[k] = donor.block_lens[k]
+    out.name = f"{base.name}+r{k}from{donor.name}"
+    return out
+
+
 @dataclasses.dataclass
 class NormRopeRows:
     """Inputs of the standalone q/k norm + rotation op: packed rows, one position each."""

@@ -1,22 +1,26 @@
 /*
  * drafter_attn.h -- C ABI of the MI355X (gfx950) drafter block-attention library.
  *
- * The operation (TensorRT-LLM PR #20532 "Share Kimi K3 FP4 modeling and add NVFP4
- * support on SM103", Conversation: the commit that adds k3_drafter_attn and
- * k3_drafter_attn_qknorm, and the next commit that adds their contracts):
+ * What is computed (TensorRT-LLM PR #20532 "Share Kimi K3 FP4 modeling and add NVFP4
+ * support on SM103", Conversation: the commit adding k3_drafter_attn and
+ * k3_drafter_attn_qknorm, and the commit after it that adds their contracts):
  *
- *   Each of up to 8 requests brings a draft block of up to 8 tokens.  Every
- *   block attends densely (no causal mask) to its request's paged context and
- *   to its own K/V, which are read from the packed qkv rows and are never
- *   written into the page pool.  GQA with 6 query heads per KV head, head_dim
- *   64, HND pages of 64 tokens.  Head layouts 6/1 and 24/4; context lengths 0
- *   to 2041 in the contract tests; page tables as dense or strided rows with
- *   padded page strides; int32 or int64 positions.  drafter_attn takes q/k that
- *   are already normalised and rotated; drafter_attn_qknorm applies the
- *   per-head q/k RMSNorm (eps 1e-5) and the NeoX rotary embedding (base 10000)
- *   inside the kernel.  Lengths, page tables and qkv are read on the device,
- *   so a call captured in a HIP graph replays correctly after those buffers
- *   are rewritten in place.
+ *   batch     R <= 8 requests with T <= 8 draft tokens each (one block per request)
+ *   heads     Hq = 6 * Hkv query heads over Hkv KV heads, head_dim 64; the layouts
+ *             the contracts test are 6/1 and 24/4
+ *   keys      for each request, its L_r context tokens, kept in HND pages of 64 tokens
+ *             named by its page-table row, followed by its b_r block tokens, whose k
+ *             and v columns are taken from the packed qkv rows (the pool is never
+ *             written)
+ *   mask      none: each block token sees every key of its own request
+ *   qknorm    drafter_attn_qknorm RMS-normalises each q and k head of the block
+ *             (eps 1e-5) and applies the NeoX rotation (base 10000) before attending;
+ *             drafter_attn expects q and k already processed
+ *   replay    the kernels read lengths, page-table rows, positions and qkv from device
+ *             memory at run time, so a call captured in a HIP graph stays correct when
+ *             those buffers are rewritten in place between replays
+ *   ranges    the contracts test lengths 0 to 2041, dense and padded page-table
+ *             strides, and int32 and int64 positions
  *
  * For request r, block token t < b_r, query head h (KV head g = h / 6):
  *
@@ -34,8 +38,11 @@
  *              [Hkv][64 slots][64 dims] (HND).  v_pool likewise, same stride
  *              (a fused [P][2][Hkv][64][64] pool is v_pool = k_pool + Hkv*4096,
  *              pool_page_stride = 2*Hkv*4096).
- *   page_table int32 [R][page_table_stride]; only the first ceil(L_r/64)
- *              entries of row r are read.  Other entries may hold anything.
+ *   page_table int32 [R][page_table_stride], all of it readable memory.  The
+ *              kernel loads the entries of each split's page range (see
+ *              drafter_attn_plan) before it has the row's length, so any entry of row
+ *              r may be loaded; only the first ceil(L_r/64) are used as page ids.  The
+ *              others may hold anything: their values are never used.
  *   out        [R*T rows][out_row_stride elements] bf16; rows t >= b_r are
  *              written as zeros.
  *   positions  int32 or int64 [R*T], read per token (row order of qkv).
@@ -97,16 +104,17 @@ enum {
 
 /*
  * Bytes of workspace a call with these sizes needs (0 for arguments outside the
- * contract).  The workspace holds one fp32 partial (running max, weight sum,
- * unnormalised output) per (request, KV head, context split) and one counter
- * per (request, KV head), each counter on its own 256-byte line.  The workspace must be 256-byte aligned (as hipMalloc
- * returns).  The counters must be zero before the first call on a workspace
- * (zero the whole buffer once after allocating it); every call leaves them zero
- * again.  Two calls in flight on one workspace race.
+ * contract, a head_dim other than 64 included).  The workspace holds one fp32
+ * partial (running max, weight sum, unnormalised output) per (request, KV head,
+ * context split) and one counter per (request, KV head), each counter on its own
+ * 256-byte line.  The workspace must be 256-byte aligned (as hipMalloc returns).
+ * The counters must be zero before the first call on a workspace (zero the whole
+ * buffer once after allocating it); every call leaves them zero again.  Two calls
+ * in flight on one workspace race.
  */
 size_t drafter_attn_workspace_bytes(int32_t num_requests, int32_t tokens_per_block,
                                     int32_t num_q_heads, int32_t num_kv_heads,
-                                    int32_t page_table_stride);
+                                    int32_t head_dim, int32_t page_table_stride);
 
 /*
  * The split-KV plan the library uses for these sizes: the page-table row is cut

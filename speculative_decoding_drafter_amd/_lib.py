@@ -21,7 +21,7 @@ c_yarnp = ctypes.POINTER(DaYarn)
 
 # name -> (restype, argtypes), in the header's order
 SIGNATURES = {
-    "drafter_attn_workspace_bytes": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32]),
+    "drafter_attn_workspace_bytes": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32]),
     "drafter_attn_plan": (ctypes.c_int, [c_i32, c_i32, c_i32, c_i32p, c_i32p]),
     "drafter_attn": (ctypes.c_int, [
         c_vp, c_i64,                  # qkv, qkv_row_stride

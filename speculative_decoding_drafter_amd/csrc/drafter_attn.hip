@@ -167,7 +167,10 @@ __device__ __forceinline__ uint64_t uniform_u64(uint64_t v) {
 // 1024*j and lands at lds_base + 1024*j + 16*lane.  sbase and lds_base are
 // wave-uniform (SGPRs / M0).  Issued from inline asm so that the compiler does
 // not treat every later LDS read as dependent on it (it would wait for all DMA in
-// flight); the page loop places its own vmcnt waits.
+// flight); the page loop places its own vmcnt waits.  The asm writes m0 without
+// declaring it (clang does not accept m0 as a clobber), which is sound only while the
+// compiler itself never uses m0 in this file's device code: a CPU test compiles the
+// device code to assembly and checks that every m0 reference is this helper's.
 __device__ __forceinline__ void dma16x4(uint32_t v0, uint32_t v1, uint32_t v2, uint32_t v3, const void* sbase,
                                         uint32_t lds_base) {
   asm volatile(
@@ -924,7 +927,8 @@ __global__ __launch_bounds__(kApThreads) void kv_append_kernel(const Params p) {
     if (tid == 0 && g == 0) flag(p.status, DA_FLAG_BLOCK_LEN);
     b = b < 1 ? 1 : T;
   }
-  if (L < 0 || L + b > p.pt_stride * kPage) {
+  // L + b could overflow for a length near INT_MAX: compare against the room left instead
+  if (L < 0 || L > p.pt_stride * kPage - b) {
     if (tid == 0 && g == 0) flag(p.status, DA_FLAG_CONTEXT_LEN);
     return;
   }
@@ -986,13 +990,19 @@ struct WsLayout {
   size_t counters, part_o, part_ml, total;
 };
 
-WsLayout ws_layout(int R, int Hkv, int S) {
+// Counters first (counter_bytes, at least R * Hkv lines of 256 bytes), then the fp32
+// partial outputs and the (max, sum) pairs, each region 256-byte aligned.
+WsLayout ws_layout_after(size_t counter_bytes, int R, int Hkv, int S) {
   WsLayout l;
   l.counters = 0;
-  l.part_o = align256(static_cast<size_t>(R) * Hkv * kCounterStride * 4);
+  l.part_o = align256(counter_bytes);
   l.part_ml = l.part_o + align256(static_cast<size_t>(R) * Hkv * S * kRows * kD * 4);
   l.total = l.part_ml + align256(static_cast<size_t>(R) * Hkv * S * kRows * 2 * 4);
   return l;
+}
+
+WsLayout ws_layout(int R, int Hkv, int S) {
+  return ws_layout_after(static_cast<size_t>(R) * Hkv * kCounterStride * 4, R, Hkv, S);
 }
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
@@ -1025,6 +1035,32 @@ struct Common {
   void* stream;
 };
 
+// Byte extents of the arrays an attention call reads (ins) and of the rows it writes.
+struct Extent {
+  const void* p;
+  size_t n;
+  const char* name;
+};
+struct Extents {
+  size_t out_n;
+  Extent ins[6];
+};
+
+Extents extents(const Common& a) {
+  const int64_t rows = static_cast<int64_t>(a.R) * a.T;
+  const int64_t width = static_cast<int64_t>(a.Hq + 2 * a.Hkv) * kD;
+  const size_t qkv_n = static_cast<size_t>(((rows - 1) * a.qkv_row_stride + width) * 2);
+  const size_t pool_n = a.page_table_stride > 0
+      ? static_cast<size_t>(((static_cast<int64_t>(a.num_pages) - 1) * a.pool_page_stride + static_cast<int64_t>(a.Hkv) * kPage * kD) * 2)
+      : 0;
+  const size_t pt_n = static_cast<size_t>(a.R) * a.page_table_stride * 4;
+  const size_t r_n = static_cast<size_t>(a.R) * 4;
+  return Extents{static_cast<size_t>(((rows - 1) * a.out_row_stride + a.Hq * kD) * 2),
+                 {{a.qkv, qkv_n, "qkv"}, {a.k_pool, pool_n, "k_pool"}, {a.v_pool, pool_n, "v_pool"},
+                  {a.page_table, pt_n, "page_table"}, {a.context_lens, r_n, "context_lens"},
+                  {a.block_lens, r_n, "block_lens"}}};
+}
+
 int check_sizes(int R, int T, int Hq, int Hkv, int head_dim, int page_size, int stride) {
   if (head_dim != kD) return fail(DA_EUNSUPPORTED, "head_dim must be 64");
   if (page_size != kPage) return fail(DA_EUNSUPPORTED, "page_size must be 64");
@@ -1037,7 +1073,8 @@ int check_sizes(int R, int T, int Hq, int Hkv, int head_dim, int page_size, int 
   return DA_OK;
 }
 
-int validate(const Common& a, size_t need_ws) {
+// Every check of the attention arguments except those of the workspace.
+int validate_args(const Common& a) {
   int rc = check_sizes(a.R, a.T, a.Hq, a.Hkv, a.head_dim, a.page_size, a.page_table_stride);
   if (rc != DA_OK) return rc;
   if (!a.qkv || !a.out || !a.context_lens) return fail(DA_EINVAL, "qkv, out and context_lens must be non-NULL");
@@ -1060,36 +1097,33 @@ int validate(const Common& a, size_t need_ws) {
       !aligned_to(a.status_word, 4))
     return fail(DA_EINVAL, "page_table, context_lens, block_lens and status_word must be 4-byte aligned");
   if (!(std::isfinite(a.scale) && a.scale > 0.f)) return fail(DA_EINVAL, "scale must be finite and > 0");
-  if (!a.workspace || a.workspace_bytes < need_ws)
-    return fail(DA_EWORKSPACE, "workspace missing or smaller than drafter_attn_workspace_bytes()");
-  if (reinterpret_cast<uintptr_t>(a.workspace) & 255u) return fail(DA_EWORKSPACE, "workspace must be 256-byte aligned");
-  // aliasing: out must not overlap any input or the workspace; the workspace no input
-  const int64_t rows = static_cast<int64_t>(a.R) * a.T;
-  const size_t out_n = static_cast<size_t>(((rows - 1) * a.out_row_stride + a.Hq * kD) * 2);
-  const size_t qkv_n = static_cast<size_t>(((rows - 1) * a.qkv_row_stride + width) * 2);
-  const size_t pool_n = a.page_table_stride > 0
-      ? static_cast<size_t>(((static_cast<int64_t>(a.num_pages) - 1) * a.pool_page_stride + static_cast<int64_t>(a.Hkv) * kPage * kD) * 2)
-      : 0;
-  const size_t pt_n = static_cast<size_t>(a.R) * a.page_table_stride * 4;
-  const size_t r_n = static_cast<size_t>(a.R) * 4;
-  struct Rng { const void* p; size_t n; const char* name; } ins[] = {
-      {a.qkv, qkv_n, "qkv"}, {a.k_pool, pool_n, "k_pool"}, {a.v_pool, pool_n, "v_pool"},
-      {a.page_table, pt_n, "page_table"}, {a.context_lens, r_n, "context_lens"},
-      {a.block_lens, r_n, "block_lens"}};
-  for (const Rng& in : ins) {
-    if (overlaps(a.out, out_n, in.p, in.n)) return fail(DA_EINVAL, std::string("out overlaps ") + in.name);
-    if (overlaps(a.workspace, need_ws, in.p, in.n)) return fail(DA_EINVAL, std::string("workspace overlaps ") + in.name);
-  }
-  if (overlaps(a.out, out_n, a.workspace, need_ws)) return fail(DA_EINVAL, "out overlaps workspace");
-  if (a.status_word && (overlaps(a.status_word, 4, a.out, out_n) || overlaps(a.status_word, 4, a.workspace, need_ws)))
-    return fail(DA_EINVAL, "status_word overlaps out or workspace");
+  const Extents x = extents(a);
+  for (const Extent& in : x.ins)
+    if (overlaps(a.out, x.out_n, in.p, in.n)) return fail(DA_EINVAL, std::string("out overlaps ") + in.name);
+  if (a.status_word && overlaps(a.status_word, 4, a.out, x.out_n)) return fail(DA_EINVAL, "status_word overlaps out");
   return DA_OK;
 }
 
-Params make_params(const Common& a, const Plan& plan) {
+// validate_args, then the caller's workspace: present, large enough, 256-byte aligned,
+// overlapping no input, out or the status word.
+int validate(const Common& a, size_t need_ws) {
+  int rc = validate_args(a);
+  if (rc != DA_OK) return rc;
+  if (!a.workspace || a.workspace_bytes < need_ws)
+    return fail(DA_EWORKSPACE, "workspace missing or smaller than drafter_attn_workspace_bytes()");
+  if (reinterpret_cast<uintptr_t>(a.workspace) & 255u) return fail(DA_EWORKSPACE, "workspace must be 256-byte aligned");
+  const Extents x = extents(a);
+  for (const Extent& in : x.ins)
+    if (overlaps(a.workspace, need_ws, in.p, in.n)) return fail(DA_EINVAL, std::string("workspace overlaps ") + in.name);
+  if (overlaps(a.out, x.out_n, a.workspace, need_ws)) return fail(DA_EINVAL, "out overlaps workspace");
+  if (a.status_word && overlaps(a.status_word, 4, a.workspace, need_ws))
+    return fail(DA_EINVAL, "status_word overlaps workspace");
+  return DA_OK;
+}
+
+Params make_params(const Common& a, const Plan& plan, const WsLayout& l) {
   Params p;
   std::memset(&p, 0, sizeof(p));
-  const WsLayout l = ws_layout(a.R, a.Hkv, plan.S);
   unsigned char* ws = static_cast<unsigned char*>(a.workspace);
   p.qkv = static_cast<const uint16_t*>(a.qkv);
   p.qkv_stride = a.qkv_row_stride;
@@ -1171,13 +1205,57 @@ Rope make_rope(float rope_base, const da_yarn* y) {
   return r;
 }
 
+// The qknorm arguments (positions, norm weights, eps, base, YaRN parameters), and that
+// neither out nor the workspace (ws_n bytes at ws; none when ws is NULL) overlaps them.
+struct QkArgs {
+  const void* positions;
+  int32_t positions_dtype;
+  const void* wq;
+  const void* wk;
+  float eps, rope_base;
+  const da_yarn* yarn;
+};
+
+int validate_qk(const Common& a, const QkArgs& q, const void* ws, size_t ws_n) {
+  if (!q.positions || !q.wq || !q.wk) return fail(DA_EINVAL, "positions, q_norm_weight and k_norm_weight must be non-NULL");
+  if (q.positions_dtype != DA_POS_INT32 && q.positions_dtype != DA_POS_INT64)
+    return fail(DA_EINVAL, "positions_dtype must be DA_POS_INT32 or DA_POS_INT64");
+  if (!aligned_to(q.positions, q.positions_dtype == DA_POS_INT64 ? 8 : 4))
+    return fail(DA_EINVAL, "positions must be aligned to its element size");
+  if (!(std::isfinite(q.eps) && q.eps >= 0.f)) return fail(DA_EINVAL, "eps must be finite and >= 0");
+  if (!(std::isfinite(q.rope_base) && q.rope_base > 0.f)) return fail(DA_EINVAL, "rope_base must be finite and > 0");
+  const int rc = check_yarn(q.yarn);
+  if (rc != DA_OK) return rc;
+  if (!aligned16(q.wq) || !aligned16(q.wk)) return fail(DA_EINVAL, "q_norm_weight and k_norm_weight must be 16-byte aligned");
+  const size_t out_n = extents(a).out_n;
+  const size_t pos_n = static_cast<size_t>(a.R) * a.T * (q.positions_dtype == DA_POS_INT64 ? 8 : 4);
+  if (overlaps(a.out, out_n, q.positions, pos_n) || overlaps(a.out, out_n, q.wq, kD * 2) ||
+      overlaps(a.out, out_n, q.wk, kD * 2))
+    return fail(DA_EINVAL, "out overlaps positions or a norm weight");
+  if (overlaps(ws, ws_n, q.positions, pos_n) || overlaps(ws, ws_n, q.wq, kD * 2) || overlaps(ws, ws_n, q.wk, kD * 2))
+    return fail(DA_EINVAL, "workspace overlaps positions or a norm weight");
+  return DA_OK;
+}
+
+int launch_qk(Params p, const Plan& plan, const QkArgs& q, void* stream) {
+  p.positions = q.positions;
+  p.wq = static_cast<const uint16_t*>(q.wq);
+  p.wk = static_cast<const uint16_t*>(q.wk);
+  p.eps = q.eps;
+  p.rope = make_rope(q.rope_base, q.yarn);
+  g_last_error.clear();
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return q.positions_dtype == DA_POS_INT64 ? launch_nt<true, true>(p, plan, st) : launch_nt<true, false>(p, plan, st);
+}
+
 }  // namespace
 
 extern "C" {
 
 size_t drafter_attn_workspace_bytes(int32_t num_requests, int32_t tokens_per_block, int32_t num_q_heads,
-                                    int32_t num_kv_heads, int32_t page_table_stride) {
-  if (check_sizes(num_requests, tokens_per_block, num_q_heads, num_kv_heads, kD, kPage, page_table_stride) != DA_OK)
+                                    int32_t num_kv_heads, int32_t head_dim, int32_t page_table_stride) {
+  if (check_sizes(num_requests, tokens_per_block, num_q_heads, num_kv_heads, head_dim, kPage, page_table_stride) !=
+      DA_OK)
     return 0;
   const Plan plan = make_plan(num_requests, num_kv_heads, page_table_stride);
   return ws_layout(num_requests, num_kv_heads, plan.S).total;
@@ -1204,11 +1282,11 @@ int drafter_attn(const void* qkv, int64_t qkv_row_stride, const void* k_pool, co
                  context_lens, block_lens, num_requests, tokens_per_block, num_q_heads, num_kv_heads, head_dim,
                  page_size, scale, workspace, workspace_bytes, out, out_row_stride, status_word, stream};
   const size_t need = drafter_attn_workspace_bytes(num_requests, tokens_per_block, num_q_heads, num_kv_heads,
-                                                   page_table_stride);
+                                                   head_dim, page_table_stride);
   int rc = validate(a, need);
   if (rc != DA_OK) return rc;
   const Plan plan = make_plan(num_requests, num_kv_heads, page_table_stride);
-  Params p = make_params(a, plan);
+  Params p = make_params(a, plan, ws_layout(a.R, a.Hkv, plan.S));
   g_last_error.clear();
   return launch_nt<false, false>(p, plan, static_cast<hipStream_t>(stream));
 }
@@ -1225,41 +1303,15 @@ int drafter_attn_qknorm_yarn(const void* qkv, int64_t qkv_row_stride, const void
   const Common a{qkv, qkv_row_stride, k_pool, v_pool, pool_page_stride, num_pages, page_table, page_table_stride,
                  context_lens, block_lens, num_requests, tokens_per_block, num_q_heads, num_kv_heads, head_dim,
                  page_size, scale, workspace, workspace_bytes, out, out_row_stride, status_word, stream};
+  const QkArgs q{positions, positions_dtype, q_norm_weight, k_norm_weight, eps, rope_base, yarn};
   const size_t need = drafter_attn_workspace_bytes(num_requests, tokens_per_block, num_q_heads, num_kv_heads,
-                                                   page_table_stride);
+                                                   head_dim, page_table_stride);
   int rc = validate(a, need);
   if (rc != DA_OK) return rc;
-  if (!positions || !q_norm_weight || !k_norm_weight)
-    return fail(DA_EINVAL, "positions, q_norm_weight and k_norm_weight must be non-NULL");
-  if (positions_dtype != DA_POS_INT32 && positions_dtype != DA_POS_INT64)
-    return fail(DA_EINVAL, "positions_dtype must be DA_POS_INT32 or DA_POS_INT64");
-  if (!aligned_to(positions, positions_dtype == DA_POS_INT64 ? 8 : 4))
-    return fail(DA_EINVAL, "positions must be aligned to its element size");
-  if (!(std::isfinite(eps) && eps >= 0.f)) return fail(DA_EINVAL, "eps must be finite and >= 0");
-  if (!(std::isfinite(rope_base) && rope_base > 0.f)) return fail(DA_EINVAL, "rope_base must be finite and > 0");
-  rc = check_yarn(yarn);
+  rc = validate_qk(a, q, workspace, need);
   if (rc != DA_OK) return rc;
-  if (!aligned16(q_norm_weight) || !aligned16(k_norm_weight))
-    return fail(DA_EINVAL, "q_norm_weight and k_norm_weight must be 16-byte aligned");
-  const int64_t rows = static_cast<int64_t>(num_requests) * tokens_per_block;
-  const size_t out_n = static_cast<size_t>(((rows - 1) * out_row_stride + num_q_heads * kD) * 2);
-  const size_t pos_n = static_cast<size_t>(rows) * (positions_dtype == DA_POS_INT64 ? 8 : 4);
-  if (overlaps(out, out_n, positions, pos_n) || overlaps(out, out_n, q_norm_weight, kD * 2) ||
-      overlaps(out, out_n, k_norm_weight, kD * 2))
-    return fail(DA_EINVAL, "out overlaps positions or a norm weight");
-  if (overlaps(workspace, need, positions, pos_n) || overlaps(workspace, need, q_norm_weight, kD * 2) ||
-      overlaps(workspace, need, k_norm_weight, kD * 2))
-    return fail(DA_EINVAL, "workspace overlaps positions or a norm weight");
   const Plan plan = make_plan(num_requests, num_kv_heads, page_table_stride);
-  Params p = make_params(a, plan);
-  p.positions = positions;
-  p.wq = static_cast<const uint16_t*>(q_norm_weight);
-  p.wk = static_cast<const uint16_t*>(k_norm_weight);
-  p.eps = eps;
-  p.rope = make_rope(rope_base, yarn);
-  g_last_error.clear();
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  return positions_dtype == DA_POS_INT64 ? launch_nt<true, true>(p, plan, st) : launch_nt<true, false>(p, plan, st);
+  return launch_qk(make_params(a, plan, ws_layout(num_requests, num_kv_heads, plan.S)), plan, q, stream);
 }
 
 int drafter_attn_qknorm(const void* qkv, int64_t qkv_row_stride, const void* k_pool, const void* v_pool,
@@ -1341,11 +1393,11 @@ int drafter_paged_attn(const void* qkv, int64_t qkv_row_stride, const void* k_po
                  kv_lens, block_lens, num_requests, tokens_per_block, num_q_heads, num_kv_heads, head_dim,
                  page_size, scale, workspace, workspace_bytes, out, out_row_stride, status_word, stream};
   const size_t need = drafter_attn_workspace_bytes(num_requests, tokens_per_block, num_q_heads, num_kv_heads,
-                                                   page_table_stride);
+                                                   head_dim, page_table_stride);
   int rc = validate(a, need);
   if (rc != DA_OK) return rc;
   const Plan plan = make_plan(num_requests, num_kv_heads, page_table_stride);
-  Params p = make_params(a, plan);
+  Params p = make_params(a, plan, ws_layout(a.R, a.Hkv, plan.S));
   g_last_error.clear();
   return launch_nt<false, false, false>(p, plan, static_cast<hipStream_t>(stream));
 }

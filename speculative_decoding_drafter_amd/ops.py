@@ -30,9 +30,9 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
 
 
 def workspace_bytes(num_requests: int, tokens_per_block: int, num_q_heads: int, num_kv_heads: int,
-                    page_table_stride: int) -> int:
+                    page_table_stride: int, head_dim: int = HEAD_DIM) -> int:
     n = _lib.load().drafter_attn_workspace_bytes(num_requests, tokens_per_block, num_q_heads,
-                                                 num_kv_heads, page_table_stride)
+                                                 num_kv_heads, head_dim, page_table_stride)
     if n == 0:
         raise DrafterAttnError("sizes outside the contract")
     return int(n)
@@ -73,7 +73,7 @@ def _check(cond: bool, msg: str):
 
 
 def _common(qkv, k_pool, v_pool, page_table, context_lens, block_lens, num_q_heads, num_kv_heads,
-            tokens_per_block, out, workspace):
+            tokens_per_block, out, workspace, *, takes_workspace: bool = True):
     dev = qkv.device
     _check(dev.type == "cuda", "qkv must be a GPU tensor (there is no CPU path)")
     R = int(context_lens.shape[0]) if context_lens.dim() == 1 else -1
@@ -108,9 +108,10 @@ def _common(qkv, k_pool, v_pool, page_table, context_lens, block_lens, num_q_hea
         out = torch.empty(R * T, Hq * HEAD_DIM, dtype=torch.bfloat16, device=dev)
     _check(out.dtype == torch.bfloat16 and out.dim() == 2 and out.stride(1) == 1 and
            out.shape[0] == R * T and out.shape[1] >= Hq * HEAD_DIM, "out must be bf16 [R*T, >= Hq*64]")
-    if workspace is None:
-        workspace = make_workspace(R, T, Hq, Hkv, stride, dev)
-    _check(workspace.is_contiguous(), "workspace must be contiguous")
+    if takes_workspace:
+        if workspace is None:
+            workspace = make_workspace(R, T, Hq, Hkv, stride, dev)
+        _check(workspace.is_contiguous(), "workspace must be contiguous")
     return dict(R=R, T=T, Hq=Hq, Hkv=Hkv, stride=stride, out=out, workspace=workspace, dev=dev)
 
 

@@ -8,11 +8,11 @@
 
 int main(void) {
   int32_t splits = 0, pages = 0;
-  size_t ws = drafter_attn_workspace_bytes(8, 8, 24, 4, 512);
+  size_t ws = drafter_attn_workspace_bytes(8, 8, 24, 4, 64, 512);
   if (ws == 0 || ws % 256) { printf("bad workspace size %zu\n", ws); return 1; }
   if (drafter_attn_plan(8, 4, 512, &splits, &pages) != DA_OK) { printf("plan failed\n"); return 1; }
   if (splits < 1 || (size_t)splits * (size_t)pages < 512u) { printf("plan does not cover the row\n"); return 1; }
-  if (drafter_attn_workspace_bytes(9, 8, 6, 1, 4) != 0) { printf("R = 9 accepted\n"); return 1; }
+  if (drafter_attn_workspace_bytes(9, 8, 6, 1, 64, 4) != 0) { printf("R = 9 accepted\n"); return 1; }
   /* an attention call that fails validation before any launch (head_dim 128) */
   int rc = drafter_attn((const void*)0x10000, 512, (const void*)0x200000, (const void*)0x202000, 16384, 4,
                         (const int32_t*)0x900000, 1, (const int32_t*)0x900100, NULL, 1, 8, 6, 1, 128, 64,

@@ -58,15 +58,16 @@ def test_header_constants_match_the_pages():
 def test_workspace_bytes(lib):
     f = lib.drafter_attn_workspace_bytes
     for R, T, hkv, stride in [(1, 8, 1, 1), (8, 8, 1, 32), (8, 8, 4, 40), (8, 8, 4, 512), (3, 2, 4, 0)]:
-        n = f(R, T, 6 * hkv, hkv, stride)
+        n = f(R, T, 6 * hkv, hkv, 64, stride)
         s, p = ctypes.c_int32(), ctypes.c_int32()
         assert lib.drafter_attn_plan(R, hkv, stride, ctypes.byref(s), ctypes.byref(p)) == DA_OK
         assert n >= R * hkv * s.value * 48 * 66 * 4
         assert n % 256 == 0
-    assert f(9, 8, 6, 1, 4) == 0          # too many requests
-    assert f(1, 9, 6, 1, 4) == 0          # too many tokens
-    assert f(1, 8, 12, 1, 4) == 0         # GQA ratio
-    assert f(1, 8, 6, 1, -1) == 0
+    assert f(9, 8, 6, 1, 64, 4) == 0      # too many requests
+    assert f(1, 9, 6, 1, 64, 4) == 0      # too many tokens
+    assert f(1, 8, 12, 1, 64, 4) == 0     # GQA ratio
+    assert f(1, 8, 6, 1, 128, 4) == 0     # head_dim
+    assert f(1, 8, 6, 1, 64, -1) == 0
 
 
 def test_plan_covers_the_row_and_is_data_independent(lib):
@@ -297,3 +298,4 @@ def test_binding_rejects_malformed_yarn():
                 dict(factor=4.0, original_max_position=4096, mscale=2.0)):
         with pytest.raises(DrafterAttnError):
             _yarn(bad)
+

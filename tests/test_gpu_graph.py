@@ -5,8 +5,11 @@ int32 positions, 24/4 with int64), one qknorm call is captured into a graph
 after an eager warm-up.  Three times, the context lengths, page table, qkv,
 positions and norm weights are redrawn and rewritten in place; the replay must
 match the fp64 oracle within tolerance and an eager call on the same buffers
-bit for bit.  Lengths, page tables and qkv are read on the device, which is
-what makes the replays valid.
+bit for bit.  Then, with two or more requests, only one request's qkv rows,
+page-table row, length and positions are rewritten: the next replay must leave
+every other request's output rows bit-identical (requests isolated), change that
+request's rows, and match the oracle.  Lengths, page tables and qkv are read on
+the device, which is what makes the replays valid.
 """
 import numpy as np
 import pytest
@@ -85,7 +88,41 @@ def test_split_sweep_graph_replay(hkv, pools):
                 assert np.all(err <= 2e-2 + 2e-2 * np.abs(ref)), f"r={r} t={t} k={k}: max err {err.max():.3e}"
                 assert err.mean() <= 2e-3
                 worst = max(worst, float(err.max()))
+            if r >= 2:
+                worst = max(worst, _isolated_replay(cap, r, t, hkv, pool, pools_np))
     say(f"sweep Hkv={hkv}: worst max|err| {worst:.3e}")
+
+
+def _isolated_replay(cap: Captured, r: int, t: int, hkv: int, pool, pools_np) -> float:
+    """Rewrite one request in place between two replays; the others' rows keep their bits."""
+    k = (3 * r + t) % r
+    donor = ds.config4_cell(r, t, hkv, 5, pool=pool)
+    if int(donor.context_lens[k]) == int(cap.case.context_lens[k]):
+        donor.context_lens[k] = int(donor.context_lens[k]) // 3   # the length must change too
+        donor.positions[k * t:(k + 1) * t] = donor.context_lens[k] + torch.arange(t, dtype=donor.positions.dtype)
+    mixed = ds.splice_request(cap.case, donor, k)
+    before = cap.out.clone()
+    g, rows = cap.g, slice(k * t, (k + 1) * t)
+    g.qkv[rows].copy_(donor.qkv[rows])
+    g.page_table[k].copy_(donor.page_table[k])
+    g.context_lens[k:k + 1].copy_(donor.context_lens[k:k + 1])
+    g.positions[rows].copy_(donor.positions[rows])
+    cap.case = mixed
+    cap.graph.replay()
+    eager = cap.call(cap.out_eager, cap.ws_eager)
+    torch.cuda.synchronize()
+    mine = torch.zeros(r * t, dtype=torch.bool, device="cuda")
+    mine[rows] = True
+    assert torch.equal(cap.out[~mine], before[~mine]), f"r={r} t={t}: rewriting request {k} moved other requests"
+    assert not torch.equal(cap.out[mine], before[mine]), f"r={r} t={t}: request {k} did not change"
+    assert torch.equal(cap.out, eager), f"r={r} t={t}: isolated replay != eager"
+    got = cap.out.float().cpu().numpy().astype(np.float64)
+    ref = reference(mixed, pools_np)
+    err = np.abs(got - ref)
+    assert np.isfinite(got).all()
+    assert np.all(err <= 2e-2 + 2e-2 * np.abs(ref)), f"isolation r={r} t={t}: max err {err.max():.3e}"
+    assert err.mean() <= 2e-3
+    return float(err.max())
 
 
 def test_replay_bit_stable_2000(pools):

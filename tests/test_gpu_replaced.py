@@ -92,6 +92,21 @@ def test_replaced_path_long_context():
     replaced = paged_attn(rows, g.k_pool, g.v_pool, g.page_table, g.context_lens + case.T, **kw)
     torch.cuda.synchronize()
     check(to_np(replaced), to_np(fused), "replaced-vs-fused-32k")
+    # sampled (request, KV group) pairs of the replaced path against the fp64 definition, each
+    # on its request's 512 context pages gathered into a small pool
+    got = to_np(replaced)
+    for r, grp in ((0, 0), (5, 3), (7, 1)):
+        rws = slice(8 * r, 8 * (r + 1))
+        cols = (list(range(6 * grp * 64, 6 * (grp + 1) * 64)) + list(range((24 + grp) * 64, (25 + grp) * 64)) +
+                list(range((28 + grp) * 64, (29 + grp) * 64)))
+        ids = case.page_table[r, :512].long()
+        ref = oracle.drafter_attn_qknorm(
+            case.qkv[rws][:, cols].double().numpy(), case.k_pool[ids, grp:grp + 1].double().numpy(),
+            case.v_pool[ids, grp:grp + 1].double().numpy(), np.arange(512, dtype=np.int64)[None, :],
+            np.array([32768]), positions=case.positions[rws].numpy(),
+            q_norm_weight=case.q_norm_weight.double().numpy(), k_norm_weight=case.k_norm_weight.double().numpy(),
+            num_q_heads=6, num_kv_heads=1, tokens_per_block=8, scale=case.scale)
+        check(got[rws, 6 * grp * 64:6 * (grp + 1) * 64], ref, f"replaced-32k-r{r}-group{grp}")
 
 
 def kw_no_scale(kw):
@@ -131,3 +146,19 @@ def test_kv_append_flags_and_skips_bad_rows():
     assert changed == [int(case.page_table[1, 0])]
     assert torch.equal(g.k_pool[changed[0], 0, :62], before_k[changed[0], 0, :62])
     assert torch.equal(g.v_pool[changed[0], 0, 62:], g.qkv[4:6, 7 * 64:8 * 64])
+
+
+def test_kv_append_length_near_int_max_is_flagged():
+    # L + b would overflow int32 for a length within T of INT_MAX: the room check must still flag
+    # the request and write nothing (the fixed form compares L against the room left, stride*64 - b)
+    case = ds.with_append_room(ds.make_case(2, 4, 6, 1, [10, 62], seed=76, pool_pages=2), seed=77)
+    g = ds.to_device(case, "cuda")
+    before_k, before_v = g.k_pool.clone(), g.v_pool.clone()
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    g.context_lens[0] = 2 ** 31 - 2
+    g.context_lens[1] = 2 ** 31 - 1
+    say("append with lengths near INT_MAX")
+    _append_gpu(case, g, status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 1
+    assert torch.equal(g.k_pool, before_k) and torch.equal(g.v_pool, before_v)

@@ -75,3 +75,66 @@ def test_last_page_waits_for_every_dma_before_the_slot_is_reused():
     # must drain every DMA (vmcnt 0), not just this page's K
     loop = _page_loop(_code(open(SRC).read()))
     assert re.search(r"if \(more\) wait_vmcnt<8>\(\); else wait_vmcnt<0>\(\);", loop)
+
+
+# ---- m0: the DMA helper writes it from inline asm without declaring it (clang rejects m0 as a
+# clobber), so the compiler must never use m0 itself in this device code.  The check compiles
+# the device code to gfx950 assembly and requires every m0 reference to sit inside one of the
+# helper's asm blocks, as its `s_mov_b32 m0, s<N>` followed by the LDS DMA.
+
+def _m0_outside_asm(asm: str):
+    inside, outside, blocks = 0, [], []
+    cur = None
+    for ln in asm.splitlines():
+        if ";;#ASMSTART" in ln:
+            cur = []
+            continue
+        if ";;#ASMEND" in ln:
+            blocks.append(cur)
+            cur = None
+            continue
+        code = ln.split(";")[0].strip()
+        if cur is not None and code:
+            cur.append(code)
+        if re.search(r"\bm0\b", code):
+            if cur is None:
+                outside.append(code)
+            else:
+                inside += 1
+    bad_blocks = [b for b in blocks if any(re.search(r"\bm0\b", c) for c in b)
+                  and not (re.fullmatch(r"s_mov_b32 m0, s\d+", b[0]) and
+                           all(c.startswith(("s_nop", "global_load_lds_dwordx4")) for c in b[1:]))]
+    return inside, outside, bad_blocks
+
+
+@pytest.fixture(scope="module")
+def device_asm(tmp_path_factory):
+    import shutil
+    import subprocess
+
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(hipcc):
+        pytest.skip("hipcc not available")
+    inc = os.path.join(os.path.dirname(os.path.dirname(SRC)), "..", "include")
+    out = tmp_path_factory.mktemp("asm") / "drafter.s"
+    cmd = [hipcc, "-O3", "-std=c++17", "--offload-arch=gfx950", "--cuda-device-only", "-S",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-I", os.path.abspath(inc), "-o", str(out),
+           SRC]
+    res = subprocess.run(cmd, capture_output=True, text=True, timeout=300)
+    assert res.returncode == 0, res.stderr
+    return out.read_text()
+
+
+def test_m0_is_written_only_by_the_dma_helper(device_asm):
+    inside, outside, bad = _m0_outside_asm(device_asm)
+    assert inside > 0, "no DMA helper found in the assembly"
+    assert outside == [], f"compiler-managed m0 uses: {outside[:5]}"
+    assert bad == [], f"asm blocks touching m0 that are not the DMA helper: {bad[:2]}"
+
+
+def test_m0_lint_catches_a_compiler_use(device_asm):
+    planted = device_asm.replace(";;#ASMSTART", "\ts_mov_b32 m0, -1\n;;#ASMSTART", 1)
+    assert _m0_outside_asm(planted)[1] != []
+    # an asm block that reads m0 (whatever else it holds) is not the DMA helper's
+    planted = device_asm.replace(";;#ASMEND", "\ts_mov_b32 s0, m0\n;;#ASMEND", 1)
+    assert _m0_outside_asm(planted)[2] != []
