@@ -179,6 +179,44 @@ int drafter_attn_qknorm(const void* qkv, int64_t qkv_row_stride,
                         void* stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): drafter_attn_qknorm without
+ * the workspace arguments.  Arguments, layouts, results, errors and status flags are
+ * drafter_attn_qknorm's, bit for bit.  The split partials and arrival counters live in
+ * DA_NOALLOC_SCRATCH_BYTES of device memory that the library holds, one array per
+ * GPU, kept until the process ends; the call allocates nothing.
+ *
+ * Limit: 32768 bytes of counters plus R * Hkv * S partial slots of 12,672 bytes (S from
+ * drafter_attn_plan; each of the two partial regions rounded up to 256 bytes) must
+ * fit in DA_NOALLOC_SCRATCH_BYTES, i.e. at most 1,321 slots (8 x 8 tokens at 24/4 heads
+ * with 32k-token contexts uses 256, with 1M-token contexts 1,024).  Larger sizes return
+ * DA_EWORKSPACE before anything is launched.
+ *
+ * The first call on a device (the current device; `stream` must belong to it) looks up
+ * the array's device address and clears its counters on `stream`; it must not be under
+ * stream capture (DA_EINVAL).  Later calls may be captured.  All calls on one GPU share
+ * its array: two calls whose kernels overlap on one GPU (other streams, other host
+ * threads) race and give wrong results.
+ */
+#define DA_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+int drafter_attn_qknorm_noalloc(const void* qkv, int64_t qkv_row_stride,
+                                const void* k_pool, const void* v_pool, int64_t pool_page_stride,
+                                int32_t num_pages,
+                                const int32_t* page_table, int32_t page_table_stride,
+                                const int32_t* context_lens, const int32_t* block_lens,
+                                int32_t num_requests, int32_t tokens_per_block,
+                                int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t page_size,
+                                float scale,
+                                const void* positions, int32_t positions_dtype,
+                                const void* q_norm_weight, const void* k_norm_weight,
+                                float eps, float rope_base,
+                                void* out, int64_t out_row_stride,
+                                int32_t* status_word,
+                                void* stream);
+
+/*
  * fused_qk_norm_rope, the drafter's cell (TensorRT-LLM PR #20532, Conversation,
  * the commit adding fused_qk_norm_rope's drafter cell: head_dim 64, 6 query heads
  * per KV head, 1 to 64 tokens, eps 1e-5, base 10000, NeoX; the attention commit

@@ -9,6 +9,7 @@ from .ops import (  # noqa: F401
     DrafterAttnError,
     drafter_attn,
     drafter_attn_qknorm,
+    drafter_attn_qknorm_noalloc,
     kv_append,
     make_workspace,
     paged_attn,

@@ -65,6 +65,20 @@ SIGNATURES = {
         c_vp, c_i64,
         c_vp, c_vp,
     ]),
+    "drafter_attn_qknorm_noalloc": (ctypes.c_int, [
+        c_vp, c_i64,
+        c_vp, c_vp, c_i64, c_i32,
+        c_vp, c_i32,
+        c_vp, c_vp,
+        c_i32, c_i32, c_i32, c_i32,
+        c_i32, c_i32,
+        c_f32,
+        c_vp, c_i32,
+        c_vp, c_vp,
+        c_f32, c_f32,
+        c_vp, c_i64,                  # out, out_row_stride (no workspace: the library's scratch)
+        c_vp, c_vp,
+    ]),
     "drafter_qk_norm_rope": (ctypes.c_int, [
         c_vp, c_i64, c_i32,           # qkv, qkv_row_stride, num_tokens
         c_i32, c_i32, c_i32,          # Hq, Hkv, head_dim

@@ -33,6 +33,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "drafter_attn.h"
@@ -1250,6 +1251,55 @@ int launch_qk(Params p, const Plan& plan, const QkArgs& q, void* stream) {
 
 }  // namespace
 
+// ---------------------------------------------------------------------------------
+// scratch of the no-allocation entry point
+// ---------------------------------------------------------------------------------
+// Device memory that the library holds for callers that cannot allocate: the
+// arrival counters (a fixed region for the largest R * Hkv, so that calls of any
+// size find theirs at zero) and the split partials.  Every GPU the library runs on
+// holds its own copy until the process ends.  In host code `scratch` names a
+// host-side stand-in: its device address comes from hipGetSymbolAddress, once per
+// device, and only that address is handed to kernels.
+constexpr size_t kScratchBytes = DA_NOALLOC_SCRATCH_BYTES;
+constexpr size_t kScratchCounterBytes = static_cast<size_t>(DA_MAX_REQUESTS) * DA_MAX_KV_HEADS * kCounterStride * 4;
+static_assert(kScratchCounterBytes % 256 == 0, "scratch counters region");
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices];  // device address of `scratch` on each device, once set up
+
+// The current device's scratch.  The first call on a device looks up its address and
+// clears its counters on `stream` (ordered before the kernels that follow); that call
+// must not be under stream capture.  Afterwards every call leaves the counters zero.
+int scratch_of_current_device(void* stream, void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(DA_ELAUNCH, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(DA_ELAUNCH, "device ordinal above 63");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    e = hipStreamIsCapturing(static_cast<hipStream_t>(stream), &cap);
+    if (e != hipSuccess) return fail(DA_ELAUNCH, std::string("hipStreamIsCapturing: ") + hipGetErrorString(e));
+    if (cap != hipStreamCaptureStatusNone)
+      return fail(DA_EINVAL, "the first drafter_attn_qknorm_noalloc call on a device sets up its scratch and must "
+                             "not be captured");
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return fail(DA_ELAUNCH, std::string("hipGetSymbolAddress: ") + hipGetErrorString(e));
+    e = hipMemsetAsync(p, 0, kScratchCounterBytes, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(DA_ELAUNCH, std::string("clearing the scratch counters: ") + hipGetErrorString(e));
+    g_scratch_dev[dev] = p;
+  }
+  *ptr = g_scratch_dev[dev];
+  return DA_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 size_t drafter_attn_workspace_bytes(int32_t num_requests, int32_t tokens_per_block, int32_t num_q_heads,
@@ -1328,6 +1378,34 @@ int drafter_attn_qknorm(const void* qkv, int64_t qkv_row_stride, const void* k_p
                                   num_q_heads, num_kv_heads, head_dim, page_size, scale, positions,
                                   positions_dtype, q_norm_weight, k_norm_weight, eps, rope_base, nullptr,
                                   workspace, workspace_bytes, out, out_row_stride, status_word, stream);
+}
+
+int drafter_attn_qknorm_noalloc(const void* qkv, int64_t qkv_row_stride, const void* k_pool, const void* v_pool,
+                                int64_t pool_page_stride, int32_t num_pages, const int32_t* page_table,
+                                int32_t page_table_stride, const int32_t* context_lens, const int32_t* block_lens,
+                                int32_t num_requests, int32_t tokens_per_block, int32_t num_q_heads,
+                                int32_t num_kv_heads, int32_t head_dim, int32_t page_size, float scale,
+                                const void* positions, int32_t positions_dtype, const void* q_norm_weight,
+                                const void* k_norm_weight, float eps, float rope_base, void* out,
+                                int64_t out_row_stride, int32_t* status_word, void* stream) {
+  Common a{qkv, qkv_row_stride, k_pool, v_pool, pool_page_stride, num_pages, page_table, page_table_stride,
+           context_lens, block_lens, num_requests, tokens_per_block, num_q_heads, num_kv_heads, head_dim,
+           page_size, scale, nullptr, 0, out, out_row_stride, status_word, stream};
+  const QkArgs q{positions, positions_dtype, q_norm_weight, k_norm_weight, eps, rope_base, nullptr};
+  // every host check first: a refused call touches no device
+  int rc = validate_args(a);
+  if (rc != DA_OK) return rc;
+  rc = validate_qk(a, q, nullptr, 0);
+  if (rc != DA_OK) return rc;
+  const Plan plan = make_plan(num_requests, num_kv_heads, page_table_stride);
+  const WsLayout l = ws_layout_after(kScratchCounterBytes, num_requests, num_kv_heads, plan.S);
+  if (l.total > kScratchBytes)
+    return fail(DA_EWORKSPACE, "these sizes need " + std::to_string(l.total) + " bytes of scratch, above the " +
+                                   std::to_string(kScratchBytes) + " the no-allocation entry point holds");
+  rc = scratch_of_current_device(stream, &a.workspace);
+  if (rc != DA_OK) return rc;
+  a.workspace_bytes = kScratchBytes;
+  return launch_qk(make_params(a, plan, l), plan, q, stream);
 }
 
 int drafter_qk_norm_rope_yarn(void* qkv, int64_t qkv_row_stride, int32_t num_tokens, int32_t num_q_heads,

@@ -186,6 +186,39 @@ def drafter_attn_qknorm(qkv: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.T
     return a["out"]
 
 
+def drafter_attn_qknorm_noalloc(qkv: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                                page_table: torch.Tensor, context_lens: torch.Tensor, positions: torch.Tensor,
+                                q_norm_weight: torch.Tensor, k_norm_weight: torch.Tensor, out: torch.Tensor, *,
+                                num_q_heads: int, num_kv_heads: int, tokens_per_block: int,
+                                block_lens: Optional[torch.Tensor] = None, scale: Optional[float] = None,
+                                eps: float = 1e-5, rope_base: float = 10000.0,
+                                status: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """drafter_attn_qknorm for callers that cannot allocate: no workspace argument (the library's
+    own per-GPU scratch holds the split partials), and ``out`` must be given.  Calls whose kernels
+    overlap on one GPU race.  Returns ``out``."""
+    lib = _lib.load()
+    _check(out is not None, "out must be given (this entry point allocates nothing)")
+    a = _common(qkv, k_pool, v_pool, page_table, context_lens, block_lens, num_q_heads, num_kv_heads,
+                tokens_per_block, out, None, takes_workspace=False)
+    _check(positions.dtype in POS_DTYPES and positions.dim() == 1 and positions.numel() == a["R"] * a["T"]
+           and positions.is_contiguous() and positions.device == a["dev"], "positions must be int32/int64 [R*T]")
+    for name, wt in (("q_norm_weight", q_norm_weight), ("k_norm_weight", k_norm_weight)):
+        _check(wt.dtype == torch.bfloat16 and tuple(wt.shape) == (HEAD_DIM,) and wt.is_contiguous()
+               and wt.device == a["dev"], f"{name} must be bf16 [64]")
+    scale = 1.0 / math.sqrt(HEAD_DIM) if scale is None else float(scale)
+    if status is not None:
+        _check(status.dtype == torch.int32 and status.numel() >= 1 and status.device == a["dev"],
+               "status must be an int32 GPU tensor")
+    rc = lib.drafter_attn_qknorm_noalloc(
+        qkv.data_ptr(), qkv.stride(0), k_pool.data_ptr(), v_pool.data_ptr(), k_pool.stride(0), k_pool.shape[0],
+        _ptr(page_table) if a["stride"] else None, a["stride"], context_lens.data_ptr(), _ptr(block_lens),
+        a["R"], a["T"], a["Hq"], a["Hkv"], HEAD_DIM, PAGE, scale,
+        positions.data_ptr(), POS_DTYPES[positions.dtype], q_norm_weight.data_ptr(), k_norm_weight.data_ptr(),
+        float(eps), float(rope_base), out.data_ptr(), out.stride(0), _ptr(status), _stream(a["dev"]))
+    _raise(rc)
+    return out
+
+
 def qk_norm_rope(qkv: torch.Tensor, positions: torch.Tensor, q_norm_weight: torch.Tensor,
                  k_norm_weight: torch.Tensor, *, num_q_heads: int, num_kv_heads: int, eps: float = 1e-5,
                  rope_base: float = 10000.0, yarn: Optional[dict] = None) -> torch.Tensor:

@@ -26,6 +26,12 @@ int main(void) {
   rc = drafter_qk_norm_rope_yarn((void*)0x10000, 512, 8, 6, 1, 64, (const void*)0x900000, DA_POS_INT32,
                                  (const void*)0x900100, (const void*)0x900200, 1e-5f, 10000.0f, &bad, NULL);
   if (rc != DA_EINVAL || strstr(drafter_attn_last_error(), "yarn") == NULL) { printf("yarn rc %d\n", rc); return 1; }
+  /* the no-allocation variant refuses a head_dim of 128 before it touches any device */
+  rc = drafter_attn_qknorm_noalloc((const void*)0x10000, 512, (const void*)0x200000, (const void*)0x202000, 16384, 4,
+                                   (const int32_t*)0x900000, 1, (const int32_t*)0x900100, NULL, 1, 8, 6, 1, 128, 64,
+                                   0.125f, (const void*)0x900200, DA_POS_INT32, (const void*)0x900300,
+                                   (const void*)0x900400, 1e-5f, 10000.0f, (void*)0xB00000, 384, NULL, NULL);
+  if (rc != DA_EUNSUPPORTED) { printf("noalloc rc %d\n", rc); return 1; }
   printf("ok splits=%d pages=%d workspace=%zu flags=%d,%d,%d\n", splits, pages, ws, DA_FLAG_CONTEXT_LEN,
          DA_FLAG_PAGE_ID, DA_FLAG_BLOCK_LEN);
   return 0;

@@ -35,7 +35,7 @@ def test_header_declares_entry_points():
     assert _declared() == sorted(["drafter_attn", "drafter_attn_qknorm", "drafter_attn_workspace_bytes",
                                   "drafter_attn_plan", "drafter_attn_last_error", "drafter_qk_norm_rope",
                                   "drafter_kv_append", "drafter_paged_attn", "drafter_attn_qknorm_yarn",
-                                  "drafter_qk_norm_rope_yarn"])
+                                  "drafter_qk_norm_rope_yarn", "drafter_attn_qknorm_noalloc"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -299,3 +299,67 @@ def test_binding_rejects_malformed_yarn():
         with pytest.raises(DrafterAttnError):
             _yarn(bad)
 
+
+def _na(lib, **over):
+    """A drafter_attn_qknorm_noalloc call with fake (never dereferenced) pointers: every case here is
+    refused by a host check before the device is touched (no GPU in this environment)."""
+    a = dict(qkv=0x10000, qs=512, kp=0x200000, vp=0x202000, ps=16384, np_=4, pt=0x900000, pts=1, cl=0x900100,
+             bl=None, R=1, T=8, Hq=6, Hkv=1, hd=64, pg=64, scale=0.125, pos=0x900200, pdt=0, wq=0x900300,
+             wk=0x900400, eps=1e-5, base=10000.0, out=0xB00000, os=384, st=None)
+    a.update(over)
+    return lib.drafter_attn_qknorm_noalloc(
+        a["qkv"], a["qs"], a["kp"], a["vp"], a["ps"], a["np_"], a["pt"], a["pts"], a["cl"], a["bl"], a["R"], a["T"],
+        a["Hq"], a["Hkv"], a["hd"], a["pg"], a["scale"], a["pos"], a["pdt"], a["wq"], a["wk"], a["eps"], a["base"],
+        a["out"], a["os"], a["st"], None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(hd=128), DA_EUNSUPPORTED),
+    (dict(Hq=12), DA_EUNSUPPORTED),
+    (dict(R=9), DA_EINVAL),
+    (dict(T=0), DA_EINVAL),
+    (dict(qkv=None), DA_EINVAL),
+    (dict(out=None), DA_EINVAL),
+    (dict(qs=500), DA_EINVAL),
+    (dict(out=0x10000 + 256), DA_EINVAL),     # out overlaps qkv
+    (dict(scale=float("nan")), DA_EINVAL),
+    (dict(pos=None), DA_EINVAL),
+    (dict(pdt=2), DA_EINVAL),
+    (dict(wk=0x900402), DA_EINVAL),
+    (dict(eps=-1.0), DA_EINVAL),
+    (dict(pos=0xB00000), DA_EINVAL),          # out overlaps positions
+    # 8 requests x 16 KV heads with 1M-token rows: 8 * 16 * 32 partial slots, above the scratch
+    (dict(R=8, Hq=96, Hkv=16, pts=16384, qkv=0x1000000, qs=128 * 64, ps=16 * 4096 * 2, out=0x2000000,
+          os=96 * 64, pt=0x3000000, cl=0x3100000, pos=0x3200000, wq=0x3300000, wk=0x3300100), DA_EWORKSPACE),
+])
+def test_noalloc_refused_before_touching_the_device(lib, over, code):
+    assert _na(lib, **over) == code
+    assert _lib.last_error() != ""
+
+
+def test_noalloc_scratch_limit_in_partial_slots(lib):
+    # the header's limit: 32768 bytes of counters plus R*Hkv*S slots of 12,672 bytes (two regions
+    # rounded to 256) within DA_NOALLOC_SCRATCH_BYTES -- 1,321 slots.  Sizes whose plan needs more
+    # are refused with DA_EWORKSPACE.  Only refused sizes are called here: a size that fits would
+    # pass every host check and reach the device with these fake pointers.
+    text = open(HEADER).read()
+    cap = eval(re.search(r"#define DA_NOALLOC_SCRATCH_BYTES \((\d+u << \d+)\)", text).group(1).replace("u", ""))
+    a256 = lambda x: (x + 255) // 256 * 256
+    fits = lambda n: 32768 + a256(n * 48 * 64 * 4) + a256(n * 48 * 2 * 4) <= cap
+    assert fits(1321) and not fits(1322)
+    refused = 0
+    for R, hkv, stride in [(8, 16, 16384), (8, 16, 4096), (8, 4, 16384), (8, 4, 512), (2, 16, 16384), (8, 8, 8192),
+                           (8, 16, 256), (1, 1, 16384), (8, 16, 8192), (8, 12, 16384), (6, 16, 8192)]:
+        s, p = ctypes.c_int32(), ctypes.c_int32()
+        assert lib.drafter_attn_plan(R, hkv, stride, ctypes.byref(s), ctypes.byref(p)) == DA_OK
+        n = R * hkv * s.value
+        if (R, hkv, stride) in ((8, 4, 512), (8, 4, 16384), (8, 16, 256)):
+            assert fits(n), (R, hkv, stride, n)   # the 32k workload, 1M tokens at 24/4, 16k at 96/16
+        if fits(n):
+            continue
+        rc = _na(lib, R=R, Hq=6 * hkv, Hkv=hkv, pts=stride, qkv=0x1000000, qs=(8 * hkv) * 64,
+                 ps=hkv * 4096 * 2, out=0x2000000, os=6 * hkv * 64, pt=0x3000000, cl=0x3100000, pos=0x3200000,
+                 wq=0x3300000, wk=0x3300100)
+        assert rc == DA_EWORKSPACE and "scratch" in _lib.last_error(), (R, hkv, stride, n)
+        refused += 1
+    assert refused >= 3
