@@ -47,6 +47,9 @@ def parse():
     ap.add_argument("--large", action="store_true",
                     help="instead of the headline line: one line per large context (131k and 1M tokens, "
                          "24/4 and 96/16 heads), pools drawn on the device")
+    ap.add_argument("--mixed", action="store_true",
+                    help="instead of the headline line: the length-aware split schedule against the static plan "
+                         "alone, on mixed-length workloads (one line per workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=10.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -329,6 +332,107 @@ def ab_replaced(args):
     print(json.dumps(line), flush=True)
 
 
+MIXED = [  # (name, R, Hq, Hkv, page-table stride, lengths: list or (seed, max))
+    ("mixed lengths U[0, 32k], the 32k workload's stride", 8, 24, 4, 512, (11, 32768)),
+    ("mixed lengths U[0, 64k]", 8, 24, 4, 1024, (12, 65536)),
+    ("one 64k-token request among short ones", 8, 24, 4, 1024, [65536, 100, 0, 2000, 0, 1, 0, 64]),
+    ("lengths U[0, 2041] under a padded stride of 1024 pages", 8, 24, 4, 1024, (13, 2041)),
+    ("6/1 heads, mixed lengths U[0, 128k]", 8, 6, 1, 2048, (14, 131072)),
+    ("equal 32k contexts (the headline workload's shape)", 8, 24, 4, 512, [32768] * 8),
+]
+
+
+def balanced_plan(R, Hkv, stride, lens):
+    """(balanced?, pages per split) of the length-aware schedule for these lengths, as the
+    header documents it (reported beside the timings)."""
+    import math
+    from speculative_decoding_drafter_amd import plan
+
+    S, Ps = plan(R, Hkv, stride)
+    npg = [math.ceil(min(max(L, 0), stride * 64) / 64) for L in lens]
+    N, nmax = sum(npg), max(npg)
+    if S > 1 and Ps >= 32 and N > 0:
+        pb = max(math.ceil(N / (R * (S - 1))), math.ceil(nmax / 32))
+        pb = max(8, math.ceil(pb / 8) * 8)
+        if pb <= (3 * Ps // 4) // 8 * 8:
+            return True, pb
+    return False, Ps
+
+
+def mixed_lengths(args):
+    """The length-aware schedule against the static plan alone (the same source built with
+    DA_STATIC_PLAN_ONLY), on mixed-length workloads: interleaved rounds, cold (1 GiB read
+    before every call), one event pair per call; one JSON line per workload."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    import drafter_synth as ds
+    from speculative_decoding_drafter_amd import _lib, build
+
+    libs = {}
+    for name, path in (("length_aware", _lib.library_path()), ("static_plan", build.LIB_STATIC_PLAN)):
+        lib = ctypes.CDLL(path)
+        fn = lib.drafter_attn_qknorm
+        fn.restype, fn.argtypes = _lib.SIGNATURES["drafter_attn_qknorm"]
+        wsf = lib.drafter_attn_workspace_bytes
+        wsf.restype, wsf.argtypes = _lib.SIGNATURES["drafter_attn_workspace_bytes"]
+        libs[name] = (fn, wsf)
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    flush_out = torch.empty((), dtype=torch.float32, device="cuda")
+    for wname, R, Hq, Hkv, stride, lens in MIXED:
+        if isinstance(lens, tuple):
+            rng = np.random.default_rng(lens[0])
+            lens = [int(x) for x in rng.integers(0, lens[1] + 1, R)]
+        pages = sum(-(-L // 64) for L in lens) + 8
+        pool = ds.device_normal_pool(pages, Hkv, seed=17, device="cuda")
+        case = ds.make_case(R, 8, Hq, Hkv, lens, seed=17, stride=stride, pool_pages=pages, qknorm=True,
+                            pool_override=pool)
+        g = ds.to_device(case, "cuda")
+        out = torch.empty(R * 8, Hq * 64, dtype=torch.bfloat16, device="cuda")
+        ws = {k: torch.zeros(int(wsf(R, 8, Hq, Hkv, 64, stride)), dtype=torch.uint8, device="cuda")
+              for k, (_, wsf) in libs.items()}
+
+        def call(k):
+            fn = libs[k][0]
+            rc = fn(g.qkv.data_ptr(), g.qkv.stride(0), g.k_pool.data_ptr(), g.v_pool.data_ptr(), g.k_pool.stride(0),
+                    g.k_pool.shape[0], g.page_table.data_ptr(), stride, g.context_lens.data_ptr(), None, R, 8, Hq,
+                    Hkv, 64, 64, case.scale, g.positions.data_ptr(), 0, g.q_norm_weight.data_ptr(),
+                    g.k_norm_weight.data_ptr(), 1e-5, 10000.0, ws[k].data_ptr(), ws[k].numel(), out.data_ptr(),
+                    out.stride(0), None, torch.cuda.current_stream().cuda_stream)
+            assert rc == 0, rc
+
+        res = {k: [] for k in libs}
+        rounds = max(2, args.steps // 25)
+        for rnd in range(rounds + 1):             # round 0 is warm-up
+            for k in (list(libs) if rnd % 2 else list(libs)[::-1]):
+                evs = []
+                for _ in range(25):
+                    torch.sum(flush, dim=0, out=flush_out)
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record(); call(k); e1.record()
+                    evs.append((e0, e1))
+                torch.cuda.synchronize()
+                if rnd:
+                    res[k] += [a.elapsed_time(b) * 1e3 for a, b in evs]
+        kv = case.kv_bytes()
+        us = {k: float(np.mean(v)) for k, v in res.items()}
+        bal, ps = balanced_plan(R, Hkv, stride, lens)
+        from speculative_decoding_drafter_amd import plan
+        S, Ps = plan(R, Hkv, stride)
+        print(json.dumps({"metric": "length-aware schedule vs static plan (us/call, cold)", "workload": wname,
+                          "requests": R, "q_heads": Hq, "kv_heads": Hkv, "page_table_stride": stride,
+                          "context_lens": lens, "kv_bytes_per_call": kv, "static_plan": {"splits": S, "pages": Ps},
+                          "length_aware_plan": {"balanced": bal, "pages_per_split": ps},
+                          "us_length_aware": round(us["length_aware"], 2), "us_static_plan": round(us["static_plan"], 2),
+                          "speedup": round(us["static_plan"] / us["length_aware"], 3),
+                          "GBs_length_aware": round(kv / (us["length_aware"] * 1e-6) / 1e9, 1),
+                          "calls_each": len(res["length_aware"])}), flush=True)
+        del pool, case, g, ws, out
+        torch.cuda.empty_cache()
+
+
 def main():
     args = parse()
     if args.traffic_from:
@@ -343,6 +447,9 @@ def main():
         return
     if args.large:
         large_contexts(args)
+        return
+    if args.mixed:
+        mixed_lengths(args)
         return
     import torch
 

@@ -117,13 +117,30 @@ size_t drafter_attn_workspace_bytes(int32_t num_requests, int32_t tokens_per_blo
                                     int32_t head_dim, int32_t page_table_stride);
 
 /*
- * The split-KV plan the library uses for these sizes: the page-table row is cut
- * into *num_splits ranges of *pages_per_split pages, each processed by one
- * workgroup.  It depends only on these host values (never on device data).  On
- * the device a request uses only the ranges its context length reaches (at
- * least the first, which also holds the block's own keys), so the work follows
- * the lengths while the same inputs always take the same path: results are
- * bit-identical across reruns and graph replays.  Returns DA_OK or DA_EINVAL.
+ * The static split-KV plan for these sizes: S = *num_splits workgroups per
+ * (request, KV head), each covering Ps = *pages_per_split pages of the
+ * page-table row.  It depends only on these host values.  On the device a request
+ * uses only the ranges its context length reaches (at least the first, which also
+ * holds the block's own keys).
+ *
+ * Length-aware schedule: when S > 1 and Ps >= 32, the kernel reads every request's
+ * length and may take a balanced plan instead.  With npg_i = ceil(L_i / 64), N =
+ * sum npg_i and Pb = the smallest multiple of 8 (at least 8) that is >= ceil(N /
+ * (R (S - 1))) and >= ceil(max npg_i / 32), the balanced plan is taken when Pb <=
+ * 3 Ps / 4 (rounded down to a multiple of 8).  Request i is then cut into
+ * k_i = max(1, ceil(npg_i / Pb)) splits of Pb pages (consecutive entries, at most
+ * R * S in all) spread over the same grid of workgroups, so that long requests no
+ * longer leave most workgroups idle.  The workspace size is the same for both plans.
+ *
+ * Either way the schedule is a function of the lengths and the host sizes, so the
+ * same inputs always take the same path and the same reduction order: results are
+ * bit-identical across reruns and graph replays.  Under the static plan a request's
+ * output bits depend only on its own inputs.  Under the balanced plan they also
+ * depend on Pb, i.e. on the other requests' lengths: rewriting another request's
+ * rows, pages or positions, or its length without moving Pb, leaves them
+ * bit-identical; a length that moves Pb moves every request's split boundaries,
+ * which changes the last bits of their outputs (within rounding).
+ * Returns DA_OK or DA_EINVAL.
  */
 int drafter_attn_plan(int32_t num_requests, int32_t num_kv_heads, int32_t page_table_stride,
                       int32_t* num_splits, int32_t* pages_per_split);

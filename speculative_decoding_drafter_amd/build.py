@@ -29,19 +29,27 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build the HIP library)")
 
 
-def build_library(verbose: bool = False) -> str:
+# The same source built with the static split plan only: the reference against which
+# `bench.py --mixed` measures the length-aware schedule (nothing else loads it).
+LIB_STATIC_PLAN = os.path.join(PKG, "libdrafter_attn_static_plan.so")
+
+
+def build_library(verbose: bool = False, static_plan_only: bool = False) -> str:
     """Compile the library from source (always) and return the path of the .so."""
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-o", tmp, SRC]
+    lib = LIB_STATIC_PLAN if static_plan_only else LIB
+    tmp = lib + ".tmp"
+    extra = ["-DDA_STATIC_PLAN_ONLY"] if static_plan_only else []
+    cmd = [hipcc(), *HIPCC_FLAGS, *extra, "-I", INCLUDE, "-o", tmp, SRC]
     res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     msgs = [ln for ln in res.stdout.splitlines() if "packed-fp32-ops" not in ln]
     if res.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs), file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
     print(build_library(verbose=True))
+    print(build_library(verbose=True, static_plan_only=True))

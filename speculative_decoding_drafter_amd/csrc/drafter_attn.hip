@@ -51,6 +51,7 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kMaxSplits = 64;
 constexpr int kMaxStride = 16384;            // pages per request row (with 64 splits: <= 256 per split)
 constexpr int kMaxPagesPerSplit = 64 * kWaves;  // a wave's page ids fit one 64-lane VGPR
+constexpr int kMaxReqSplits = 32;             // balanced plan: splits per request (bounds its combine)
 constexpr int kTileBytes = kPage * kD * 2;   // one [64][64] bf16 tile, 8 KiB
 constexpr int kStageBytes = 2 * kTileBytes;  // a wave's K slot then V slot
 constexpr float kRescaleLog2 = 8.0f;         // lazy-rescale headroom (exp2 units)
@@ -119,6 +120,9 @@ struct Params {
   int32_t pt_stride;
   int32_t R, T, Hq, Hkv;
   int32_t S, Ps;
+  // Length-aware scheduling: the balanced plan is taken when the requests' pages N > 0
+  // satisfy N <= bal_n and their largest page count <= bal_npg (0, 0: never)
+  int32_t bal_n, bal_npg;
   float c;    // scale * log2(e): scores live in the exp2 domain
   float eps;
   Rope rope;
@@ -513,15 +517,15 @@ __device__ __forceinline__ u32x4 pack8(const float (&x)[8]) {
 // OWN = false is the attention of the path the fused op replaces: the block's
 // queries attend to pooled keys only (the caller appended the block to the pool and
 // passes kv lengths L + b), nothing is read from qkv but the queries.
-template <int NT, bool QKNORM, bool POS64, bool OWN = true>
+template <int NT, bool QKNORM, bool POS64, bool OWN = true, bool BAL = false>
 __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kSmemBytes];
-  const int s = blockIdx.x, g = blockIdx.y, r = blockIdx.z;
+  int s = blockIdx.x, r = blockIdx.z;
+  const int g = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int T = p.T;
   const int nrows = kG * T;
-  const int rg = r * p.Hkv + g;
 
   // ---- a1: every global load of the prologue is issued first and consumed before
   // the first page's DMA: the waits the compiler places before a use cannot tell
@@ -536,14 +540,14 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
   //
   // A split narrower than the waves (4 pages) gives its pages to the highest
   // waves, which have the least prologue work and issue their first page early.
-  const int pbeg = s * p.Ps;
-  const int wshift = p.Ps < kWaves ? kWaves - p.Ps : 0;
-  const int first = pbeg + w - wshift;
+  int pbeg = s * p.Ps;
+  int wshift = p.Ps < kWaves ? kWaves - p.Ps : 0;
+  int first = pbeg + w - wshift;
   const int row_end = min(pbeg + p.Ps, p.pt_stride);
   const int cand = (w >= wshift && first < row_end) ? (row_end - first + kWaves - 1) / kWaves : 0;
   int id = 0;
   if (lane < cand) id = p.page_table[static_cast<int64_t>(r) * p.pt_stride + first + kWaves * lane];
-  const bool own = OWN && s == 0;
+  bool own = OWN && s == 0;
   // Thread (sub, u) holds dims 8u .. 8u+7 of one head row: query row sub = 6t + h
   // of the tile (sub < 6T), or, in split 0, row j < T of the block's own K
   // (sub = 48 + j) or V (sub = 56 + j).  Rows past the block length are loaded
@@ -553,7 +557,7 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
   const int oj = (sub - 48) & (kMaxT - 1);
   const bool is_q = sub < nrows;
   const bool own_v = sub >= 48 + kMaxT;
-  const bool is_own = own && sub >= 48 && sub < 48 + 2 * kMaxT && oj < T;
+  bool is_own = own && sub >= 48 && sub < 48 + 2 * kMaxT && oj < T;
   u32x4 raw = {0u, 0u, 0u, 0u}, wraw = {0u, 0u, 0u, 0u};
   if (is_q) {
     raw = ld16(p.qkv + static_cast<int64_t>(r * T + q_t) * p.qkv_stride + (kG * g + sub - kG * q_t) * kD + 8 * u);
@@ -571,27 +575,30 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
   }
   int L = p.ctx_lens[r];
   int b = p.blk_lens ? p.blk_lens[r] : T;
+  // With the length-aware schedule compiled in, every request's length is loaded too,
+  // by scalar loads: they are only waited for after the first page's DMA (a vector load
+  // here would have to land before that DMA is issued).
+  int lens[DA_MAX_REQUESTS];
+#pragma unroll
+  for (int i = 0; i < DA_MAX_REQUESTS; ++i) lens[i] = (BAL && i < p.R) ? p.ctx_lens[i] : 0;
   asm volatile("" ::"v"(raw), "v"(wraw), "v"(pos), "v"(L), "v"(b));  // every prologue load has landed
 
   const int maxL = p.pt_stride * kPage;
-  if (L < 0 || L > maxL) {
-    if (tid == 0 && s == 0 && g == 0) flag(p.status, DA_FLAG_CONTEXT_LEN);
-    L = L < 0 ? 0 : maxL;
-  }
-  if (b < 1 || b > T) {
-    if (tid == 0 && s == 0 && g == 0) flag(p.status, DA_FLAG_BLOCK_LEN);
-    b = b < 1 ? 1 : T;
-  }
-  const int npg = (L + kPage - 1) / kPage;
-  // Length-aware: a request uses only the splits its pages reach (at least split 0,
-  // which holds the block's own keys); its other workgroups have nothing to do.  A
-  // request that fits one split is answered by that split directly.
-  const int s_used = max(1, (npg + p.Ps - 1) / p.Ps);
-  if (s >= s_used) return;
-  const int pend = min(npg, pbeg + p.Ps);
+  int L_in = L, b_in = b;  // as loaded, for the status flags
+  L = L < 0 ? 0 : (L > maxL ? maxL : L);
+  b = b < 1 ? 1 : (b > T ? T : b);
+  int npg = (L + kPage - 1) / kPage;
+  // A request uses only the splits its pages reach (at least split 0, which holds the
+  // block's own keys); its other workgroups have nothing to do (unless the balanced
+  // plan below gives them work).  A request that fits one split is answered by that
+  // split directly.
+  int ps = p.Ps;
+  int s_used = max(1, (npg + ps - 1) / ps);
+  int slot0 = (r * p.Hkv + g) * p.S;  // the first partial slot of (r, g)
+  int pend = min(npg, pbeg + ps);
   // the block's own keys go to a wave with the fewest pages of this split
-  const int own_wave = (max(0, pend - pbeg) + wshift) & (kWaves - 1);
-  const int cnt = (w >= wshift && first < pend) ? (pend - first + kWaves - 1) / kWaves : 0;
+  int own_wave = (max(0, pend - pbeg) + wshift) & (kWaves - 1);
+  int cnt = (w >= wshift && first < pend) ? (pend - first + kWaves - 1) / kWaves : 0;
   if (lane < cnt && (id < 0 || id >= p.num_pages)) {
     flag(p.status, DA_FLAG_PAGE_ID);
     id = id < 0 ? 0 : p.num_pages - 1;
@@ -610,6 +617,108 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
   if (early_dma && cnt > 0) {
     stage_tile<false>(p.kpool + page_off(0), lds_k, doff);
     stage_tile<true>(p.vpool + page_off(0), lds_v, doff);
+  }
+
+  // ---- length-aware split scheduling (BAL), decided while the first pages are in
+  // flight.  Every workgroup derives the same schedule from the lengths (device data)
+  // and the host sizes, so the same inputs always take the same path and the same
+  // reduction order (bit-identical reruns and replays).  Static plan (above):
+  // workgroup (x, g, z) takes split x of request z, splits of Ps pages.  Balanced
+  // plan: the N pages of all requests are cut into about R*(S-1) splits of Pb pages
+  // (a multiple of 8, at least ceil(max npg / kMaxReqSplits)); request i takes
+  // max(1, ceil(npg_i / Pb)) consecutive entries, at most R*S in all, and workgroup
+  // (x, g, z) takes entry x + S*z of KV head g.  The balanced plan is taken only when
+  // it puts at most 3/4 of the pages on a workgroup (Pb <= 3 Ps / 4), i.e. when long
+  // requests would otherwise leave many workgroups idle.  It then costs one more round
+  // trip: the
+  // workgroup loads its balanced split's page ids and rows, and the static split's
+  // first page, already in flight, is drained and dropped.
+  bool balanced = false;
+  if (BAL) {
+    int N = 0, npg_max = 0;
+#pragma unroll
+    for (int i = 0; i < DA_MAX_REQUESTS; ++i) {
+      const int n = ((lens[i] < 0 ? 0 : (lens[i] > maxL ? maxL : lens[i])) + kPage - 1) / kPage;
+      N += n;
+      npg_max = max(npg_max, n);
+    }
+    // Pb <= 3 Ps / 4 exactly when both bounds hold (thresholds from the host)
+    if (__builtin_expect(N > 0 && N <= p.bal_n && npg_max <= p.bal_npg, 0)) {
+      balanced = true;
+      // lane i < R: request i's length and page count
+      int Li = 0;
+#pragma unroll
+      for (int i = 0; i < DA_MAX_REQUESTS; ++i) Li = lane == i ? lens[i] : Li;
+      const int npg_l = ((Li < 0 ? 0 : (Li > maxL ? maxL : Li)) + kPage - 1) / kPage;
+      const int X = p.R * (p.S - 1);
+      const int pb = max((N + X - 1) / X, (npg_max + kMaxReqSplits - 1) / kMaxReqSplits);
+      ps = max(kWaves, (pb + kWaves - 1) / kWaves * kWaves);
+      const int k_l = lane < p.R ? max(1, (npg_l + ps - 1) / ps) : 0;
+      const int e = blockIdx.x + p.S * blockIdx.z;
+      int base = 0, rr = -1;
+#pragma nounroll
+      for (int i = 0; i < p.R; ++i) {
+        const int k = __builtin_amdgcn_readlane(k_l, i);
+        if (rr < 0 && e < base + k) {
+          rr = i;
+          s = e - base;
+          s_used = k;
+          slot0 = g * p.R * p.S + base;
+        }
+        base += k;
+      }
+      if (rr < 0) {  // past the schedule's last entry
+        wait_vmcnt<0>();
+        return;
+      }
+      r = rr;
+      L_in = __builtin_amdgcn_readlane(Li, r);
+      L = L_in < 0 ? 0 : (L_in > maxL ? maxL : L_in);
+      npg = __builtin_amdgcn_readlane(npg_l, r);
+      pbeg = s * ps;
+      wshift = 0;
+      first = pbeg + w;
+      pend = min(npg, pbeg + ps);
+      own_wave = (pend - pbeg) & (kWaves - 1);
+      cnt = first < pend ? (pend - first + kWaves - 1) / kWaves : 0;
+      own = OWN && s == 0;
+      is_own = own && sub >= 48 && sub < 48 + 2 * kMaxT && oj < T;
+      id = 0;
+      if (lane < cnt) id = p.page_table[static_cast<int64_t>(r) * p.pt_stride + first + kWaves * lane];
+      raw = wraw = u32x4{0u, 0u, 0u, 0u};
+      if (is_q) {
+        raw = ld16(p.qkv + static_cast<int64_t>(r * T + q_t) * p.qkv_stride + (kG * g + sub - kG * q_t) * kD + 8 * u);
+        if (QKNORM) wraw = ld16(p.wq + 8 * u);
+      } else if (is_own) {
+        raw = ld16(p.qkv + static_cast<int64_t>(r * T + oj) * p.qkv_stride +
+                   (own_v ? p.Hq + p.Hkv + g : p.Hq + g) * kD + 8 * u);
+        if (QKNORM && !own_v) wraw = ld16(p.wk + 8 * u);
+      }
+      if (QKNORM && tid < T * 32) {
+        const int t = tid >> 5;
+        pos = POS64 ? static_cast<const int64_t*>(p.positions)[r * T + t]
+                    : static_cast<int64_t>(static_cast<const int32_t*>(p.positions)[r * T + t]);
+      }
+      b = p.blk_lens ? p.blk_lens[r] : T;
+      wait_vmcnt<0>();  // these loads, and the static split's first page (its slot is reused)
+      asm volatile("" ::"v"(raw), "v"(wraw), "v"(pos), "v"(b), "v"(id));
+      b_in = b;
+      b = b < 1 ? 1 : (b > T ? T : b);
+      if (lane < cnt && (id < 0 || id >= p.num_pages)) {
+        flag(p.status, DA_FLAG_PAGE_ID);
+        id = id < 0 ? 0 : p.num_pages - 1;
+      }
+      if (early_dma && cnt > 0) {
+        stage_tile<false>(p.kpool + page_off(0), lds_k, doff);
+        stage_tile<true>(p.vpool + page_off(0), lds_v, doff);
+      }
+    }
+  }
+  if (!balanced && s >= s_used) return;
+  const int rg = r * p.Hkv + g;
+  if (tid == 0 && s == 0 && g == 0) {  // request r's first split reports its length and block length
+    if (L_in < 0 || L_in > maxL) flag(p.status, DA_FLAG_CONTEXT_LEN);
+    if (b_in < 1 || b_in > T) flag(p.status, DA_FLAG_BLOCK_LEN);
   }
 
   float2* cs = reinterpret_cast<float2*>(smem + kOffCS);
@@ -779,7 +888,7 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
   // The partial is published with device-scope stores (coherent across the
   // XCDs' L2s without a cache write-back), completed before the counter
   // increment; the last workgroup reads it back with device-scope loads.
-  const int rgs = rg * p.S + s;
+  const int rgs = slot0 + s;
   if (row_thread) {
     const __amdgpu_buffer_rsrc_t po = dev_rsrc(p.part_o + static_cast<int64_t>(rgs) * kRows * kD, kRows * kD * 4);
     const int off = (row * kD + 4 * oc) * 4;
@@ -809,9 +918,8 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
   // split order.  Memory round trips dominate here, so every load of a chunk of
   // splits is issued before its first use: one round trip when S <= kChunk.
   const int S = s_used;
-  const int64_t slot0 = static_cast<int64_t>(rg) * p.S;  // the group's first partial slot
-  const __amdgpu_buffer_rsrc_t pm = dev_rsrc(p.part_ml + slot0 * kRows * 2, S * kRows * 2 * 4);
-  const __amdgpu_buffer_rsrc_t po = dev_rsrc(p.part_o + slot0 * kRows * kD, S * kRows * kD * 4);
+  const __amdgpu_buffer_rsrc_t pm = dev_rsrc(p.part_ml + static_cast<int64_t>(slot0) * kRows * 2, S * kRows * 2 * 4);
+  const __amdgpu_buffer_rsrc_t po = dev_rsrc(p.part_o + static_cast<int64_t>(slot0) * kRows * kD, S * kRows * kD * 4);
   constexpr int kChunk = 8;
   f32x2 ml[kChunk];
   f32x4 ov[kChunk][2];
@@ -1151,6 +1259,21 @@ Params make_params(const Common& a, const Plan& plan, const WsLayout& l) {
   p.Hkv = a.Hkv;
   p.S = plan.S;
   p.Ps = plan.Ps;
+  // the balanced plan is taken when Ps >= 32 (4 pages per wave) and its splits of Pb
+  // pages (a multiple of 8) hold at most M = 3 Ps / 4 (rounded down to a multiple of
+  // 8), i.e. ceil(N / (R (S-1))) and ceil(max npg / 32) are both at most M: a smaller
+  // saving does not pay for the extra round trip.  (A build with DA_STATIC_PLAN_ONLY
+  // defined keeps the static plan everywhere: the reference the scheduling is measured
+  // against.)
+#ifndef DA_STATIC_PLAN_ONLY
+  if (plan.S > 1 && plan.Ps >= 4 * kWaves) {
+#else
+  if (false) {
+#endif
+    const int M = 3 * plan.Ps / 4 / kWaves * kWaves;
+    p.bal_n = a.R * (plan.S - 1) * M;
+    p.bal_npg = kMaxReqSplits * M;
+  }
   p.c = static_cast<float>(static_cast<double>(a.scale) * 1.4426950408889634);  // log2(e)
   return p;
 }
@@ -1158,7 +1281,12 @@ Params make_params(const Common& a, const Plan& plan, const WsLayout& l) {
 template <int NT, bool QK, bool P64, bool OWN>
 int launch_t(const Params& p, const Plan& plan, hipStream_t stream) {
   dim3 grid(plan.S, p.Hkv, p.R);
-  hipLaunchKernelGGL((drafter_attn_kernel<NT, QK, P64, OWN>), grid, dim3(kThreads), 0, stream, p);
+  // the length-aware schedule is compiled in only where the plan leaves it room: its
+  // code costs the static path 0.4 us even where it is never taken
+  if (p.bal_n > 0)
+    hipLaunchKernelGGL((drafter_attn_kernel<NT, QK, P64, OWN, true>), grid, dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((drafter_attn_kernel<NT, QK, P64, OWN, false>), grid, dim3(kThreads), 0, stream, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(DA_ELAUNCH, std::string("launch failed: ") + hipGetErrorString(e));
   return DA_OK;
