@@ -50,6 +50,9 @@ def parse():
     ap.add_argument("--mixed", action="store_true",
                     help="instead of the headline line: the length-aware split schedule against the static plan "
                          "alone, on mixed-length workloads (one line per workload)")
+    ap.add_argument("--phases", action="store_true",
+                    help="instead of the headline line: phase timestamps of cold calls (measurement build with "
+                         "DA_PHASE_TRACE), one line per workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=10.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -433,6 +436,94 @@ def mixed_lengths(args):
         torch.cuda.empty_cache()
 
 
+def phases(args):
+    """Where a cold call's time goes: the phase timestamps of the measurement build
+    (DA_PHASE_TRACE; per workgroup, see the kernel source), for the four configurations and
+    two mixed-length workloads.  For each workload, five calls each after the 1 GiB read;
+    every figure is the median over those calls of a per-call statistic, in us from the
+    first wave's start (100 MHz counter)."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    import drafter_synth as ds
+    from speculative_decoding_drafter_amd import _lib, build, plan
+
+    lib = ctypes.CDLL(build.LIB_PHASES)
+    fns = {}
+    for k in ("drafter_attn", "drafter_attn_qknorm"):
+        fn = getattr(lib, k)
+        fn.restype, fn.argtypes = _lib.SIGNATURES[k]
+        fns[k] = fn
+    wsf = lib.drafter_attn_workspace_bytes
+    wsf.restype, wsf.argtypes = _lib.SIGNATURES["drafter_attn_workspace_bytes"]
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    flush_out = torch.empty((), dtype=torch.float32, device="cuda")
+    work = [(WORKLOADS[n], ds.make_config(n)) for n in (1, 2, 3, 5)]
+    for wname, R, Hq, Hkv, stride, lens in MIXED[1:3]:
+        if isinstance(lens, tuple):
+            lens = [int(x) for x in np.random.default_rng(lens[0]).integers(0, lens[1] + 1, R)]
+        pages = sum(-(-L // 64) for L in lens) + 8
+        work.append((wname, ds.make_case(R, 8, Hq, Hkv, lens, seed=17, stride=stride, pool_pages=pages, qknorm=True,
+                                          pool_override=ds.device_normal_pool(pages, Hkv, seed=17, device="cuda"))))
+    for wname, case in work:
+        g = ds.to_device(case, "cuda")
+        S, Ps = plan(case.R, case.Hkv, case.stride)
+        ngroups = S * case.Hkv * case.R
+        trace = torch.zeros(ngroups * 64, dtype=torch.int64, device="cuda")
+        ws = torch.zeros(int(wsf(case.R, case.T, case.Hq, case.Hkv, 64, case.stride)), dtype=torch.uint8,
+                         device="cuda")
+        out = torch.empty(case.R * case.T, case.Hq * 64, dtype=torch.bfloat16, device="cuda")
+
+        def call():
+            head = (g.qkv.data_ptr(), g.qkv.stride(0), g.k_pool.data_ptr(), g.v_pool.data_ptr(), g.k_pool.stride(0),
+                    g.k_pool.shape[0], g.page_table.data_ptr() if case.stride else None, case.stride,
+                    g.context_lens.data_ptr(), None, case.R, case.T, case.Hq, case.Hkv, 64, 64, case.scale)
+            tail = (ws.data_ptr(), ws.numel(), out.data_ptr(), out.stride(0), trace.data_ptr(),
+                    torch.cuda.current_stream().cuda_stream)
+            if case.qknorm:
+                mid = (g.positions.data_ptr(), 0 if g.positions.dtype == torch.int32 else 1,
+                       g.q_norm_weight.data_ptr(), g.k_norm_weight.data_ptr(), case.eps, case.rope_base)
+                assert fns["drafter_attn_qknorm"](*head, *mid, *tail) == 0
+            else:
+                assert fns["drafter_attn"](*head, *tail) == 0
+
+        stats = []
+        for it in range(8):
+            trace.zero_()
+            torch.sum(flush, dim=0, out=flush_out)
+            call()
+            torch.cuda.synchronize()
+            if it < 3:  # warm-up calls
+                continue
+            d = trace.view(ngroups, 64).cpu().numpy().astype(np.int64)
+            st = d[:, 0:8]
+            t0 = st[st > 0].min()
+            us = lambda x: (np.asarray(x, dtype=np.float64) - t0) / 100.0
+            pos = lambda a: a[a > 0]
+            ends = d[:, 46]
+            last = int(np.argmax(ends))
+            early = d[:, 22:24][d[:, 22:24] > 0]  # waves 6-7 issue their first page before the prologue
+            row = {"prologue_loads_landed": np.median(us(pos(d[:, 8:16]))),
+                   "first_dma_issued_waves_6_7": np.median(us(early)) if early.size else float("nan"),
+                   "first_dma_issued_all_waves": np.median(us(pos(d[:, 16:24]))),
+                   "prologue_barrier": np.median(us(pos(d[:, 47]))),
+                   "first_k_tile_landed": np.median(us(pos(d[:, 24:32]))),
+                   "loop_end_median": np.median(us(pos(d[:, 32:40]))),
+                   "loop_end_last": us(pos(d[:, 32:40])).max(),
+                   "end": us(ends[last])}
+            for k, name in ((41, "last_group_merge_barrier"), (42, "last_group_merged"),
+                            (43, "last_group_published"), (44, "last_group_counter"),
+                            (45, "last_group_combine_weights")):
+                row[name] = us(d[last, k]) if d[last, k] > 0 else float("nan")
+            stats.append(row)
+        med = {k: round(float(np.median([r[k] for r in stats])), 2) for k in stats[0]}
+        print(json.dumps({"metric": "phase timestamps of a cold call (us from the first wave's start, median of 5 "
+                                    "calls)", "workload": wname, "splits": S, "pages_per_split": Ps,
+                          "context_lens": case.context_lens.tolist(), "phases_us": med}), flush=True)
+
+
 def main():
     args = parse()
     if args.traffic_from:
@@ -450,6 +541,9 @@ def main():
         return
     if args.mixed:
         mixed_lengths(args)
+        return
+    if args.phases:
+        phases(args)
         return
     import torch
 
@@ -568,7 +662,10 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "traffic": None if args.hot else measured_traffic(args.config),
-                     "kernel": "drafter_attn_kernel<3,true,false,true>" if case.qknorm else "drafter_attn_kernel<3,false,false,true>"},
+                     "kernel": "drafter_attn_kernel<%d,%s,%s,true,%s>" % (
+                         (6 * case.T + 15) // 16, str(case.qknorm).lower(),
+                         str(case.qknorm and case.positions.dtype == torch.int64).lower(),
+                         str(S > 1 and Ps >= 32).lower())},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(case, args.cpu_budget_s)

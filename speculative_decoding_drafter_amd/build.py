@@ -29,16 +29,20 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build the HIP library)")
 
 
-# The same source built with the static split plan only: the reference against which
-# `bench.py --mixed` measures the length-aware schedule (nothing else loads it).
+# Measurement builds of the same source, loaded only by bench.py: the static split
+# plan alone (the reference `bench.py --mixed` measures the length-aware schedule
+# against) and the kernels with phase timestamps (`bench.py --phases`).
 LIB_STATIC_PLAN = os.path.join(PKG, "libdrafter_attn_static_plan.so")
+LIB_PHASES = os.path.join(PKG, "libdrafter_attn_phases.so")
+VARIANTS = {None: (LIB, []), "static_plan": (LIB_STATIC_PLAN, ["-DDA_STATIC_PLAN_ONLY"]),
+            "phases": (LIB_PHASES, ["-DDA_PHASE_TRACE"])}
 
 
-def build_library(verbose: bool = False, static_plan_only: bool = False) -> str:
-    """Compile the library from source (always) and return the path of the .so."""
-    lib = LIB_STATIC_PLAN if static_plan_only else LIB
+def build_library(verbose: bool = False, variant: str = None) -> str:
+    """Compile the library (or a measurement build of it) from source, always, and
+    return the path of the .so."""
+    lib, extra = VARIANTS[variant]
     tmp = lib + ".tmp"
-    extra = ["-DDA_STATIC_PLAN_ONLY"] if static_plan_only else []
     cmd = [hipcc(), *HIPCC_FLAGS, *extra, "-I", INCLUDE, "-o", tmp, SRC]
     res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     msgs = [ln for ln in res.stdout.splitlines() if "packed-fp32-ops" not in ln]
@@ -51,5 +55,5 @@ def build_library(verbose: bool = False, static_plan_only: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    print(build_library(verbose=True))
-    print(build_library(verbose=True, static_plan_only=True))
+    for v in VARIANTS:
+        print(build_library(verbose=True, variant=v))

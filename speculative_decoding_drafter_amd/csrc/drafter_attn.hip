@@ -434,8 +434,36 @@ __device__ __forceinline__ void attend_page(const unsigned char* kt, const unsig
   }
 }
 
+// Phase timestamps for measurement builds (DA_PHASE_TRACE defined; the product build
+// compiles them out): 64 u64 slots per workgroup, at (uint64_t*)status_word + 64 * the
+// workgroup's linear index, each a reading of the 100 MHz real-time counter:
+//   [w] wave w starts, [8+w] its prologue loads have landed, [16+w] it has issued its
+//   first page's DMA, [24+w] that page's K tile has landed, [32+w] its page loop ends,
+//   [40] XCC id, [41] after the merge barrier, [42] merged, [43] partial published,
+//   [44] counter taken, [45] combine weights done, [46] output stored, [47] after the
+//   prologue barrier.  The status flags are off in such builds.
+#ifdef DA_PHASE_TRACE
+#define DA_STAMP(slot, cond)                                                              \
+  do {                                                                                   \
+    const uint64_t da_t = __builtin_amdgcn_s_memrealtime();                             \
+    if (cond) da_trace[slot] = da_t;                                                      \
+  } while (0)
+#define DA_TRACE_BASE(p)                                                                  \
+  uint64_t* da_trace = reinterpret_cast<uint64_t*>((p).status) +                          \
+                       64 * (blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z))
+#else
+#define DA_STAMP(slot, cond) \
+  do {                       \
+  } while (0)
+#define DA_TRACE_BASE(p) \
+  do {                   \
+  } while (0)
+#endif
+
 __device__ __forceinline__ void flag(int32_t* status, int bit) {
+#ifndef DA_PHASE_TRACE
   if (status) atomicOr(status, bit);
+#endif
 }
 
 // (cos, sin) of the NeoX angle pos * f_i for frequency i < 32, f_i = base^(-2i/64):
@@ -526,6 +554,8 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int T = p.T;
   const int nrows = kG * T;
+  DA_TRACE_BASE(p);
+  DA_STAMP(w, lane == 0);
 
   // ---- a1: every global load of the prologue is issued first and consumed before
   // the first page's DMA: the waits the compiler places before a use cannot tell
@@ -582,6 +612,7 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
 #pragma unroll
   for (int i = 0; i < DA_MAX_REQUESTS; ++i) lens[i] = (BAL && i < p.R) ? p.ctx_lens[i] : 0;
   asm volatile("" ::"v"(raw), "v"(wraw), "v"(pos), "v"(L), "v"(b));  // every prologue load has landed
+  DA_STAMP(8 + w, lane == 0);
 
   const int maxL = p.pt_stride * kPage;
   int L_in = L, b_in = b;  // as loaded, for the status flags
@@ -761,7 +792,9 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
     stage_tile<false>(p.kpool + page_off(0), lds_k, doff);
     stage_tile<true>(p.vpool + page_off(0), lds_v, doff);
   }
+  DA_STAMP(16 + w, lane == 0);
   __syncthreads();  // the query tile, rotation table and own-block rows are in LDS
+  DA_STAMP(47, tid == 0);
 
   const unsigned char* qt = smem + kOffQ;
   f32x4 o[NT][4];
@@ -787,6 +820,7 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
     for (int i = 0; i < cnt; ++i) {
       const bool more = i + 1 < cnt;
       wait_vmcnt<8>();  // this page's K landed (its V may still be in flight)
+      DA_STAMP(24 + w, lane == 0 && i == 0);
       auto k_read = [&]() {
         if (more) {
           wait_lds_reads();
@@ -807,6 +841,10 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
     }
   }
 
+  DA_STAMP(32 + w, lane == 0);
+#ifdef DA_PHASE_TRACE
+  if (tid == 0) da_trace[40] = __builtin_amdgcn_s_getreg(0xF814) & 0xF;  // XCC id
+#endif
   // ---- merge the waves (fixed order).  Each wave leaves its running maxima and
   // sums and its unnormalised output in LDS -- the output inside its own page
   // slot, which it no longer reads -- and after one barrier each thread owns one
@@ -835,6 +873,7 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
             o[nt][md];
   }
   __syncthreads();
+  DA_STAMP(41, tid == 0);
 
   // query row (6t + h) and dims 4*oc .. 4*oc+3 and 32+4*oc .. 32+4*oc+3: each
   // 16-byte access of a wave's 8 threads of a row then covers one whole 128-byte
@@ -873,6 +912,7 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
   const int t_row = row / kG;
   uint16_t* out_row = p.out + static_cast<int64_t>(r * T + t_row) * p.out_stride + (kG * g + row - kG * t_row) * kD +
                       4 * oc;
+  DA_STAMP(42, tid == 0);
   if (s_used == 1) {
     // a single split: its merged state is the answer (l_wg > 0 unless there is no
     // key at all, possible only without the block's own keys: zero rows then)
@@ -883,6 +923,7 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
       for (int j = 0; j < 8; ++j) x[j] = (t_row < b) ? acc[j] * inv : 0.f;
       store_out8(out_row, x);
     }
+    DA_STAMP(46, tid == 0);
     return;
   }
   // The partial is published with device-scope stores (coherent across the
@@ -903,6 +944,7 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
   // ---- a11/a12: the last workgroup of (r, g) merges the splits
   wait_vmcnt<0>();  // this thread's partial stores are complete (visible at device scope)
   __syncthreads();
+  DA_STAMP(43, tid == 0);
   int* last = reinterpret_cast<int*>(smem + kOffFlag);
   if (tid == 0) {
     uint32_t* ctr = p.counters + kCounterStride * rg;
@@ -912,6 +954,7 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
     *last = is_last;
   }
   __syncthreads();
+  DA_STAMP(44, tid == 0);
   if (!*last || !row_thread) return;
 
   // Thread (row, oc) merges its row's S partials (the splits this request used) in
@@ -941,6 +984,7 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
 #pragma unroll
   for (int j = 0; j < kChunk; ++j) m_all = fmaxf(m_all, ml[j][0]);
   for (int k = kChunk; k < S; ++k) m_all = fmaxf(m_all, ld_dev_b64(pm, (k * kRows + row) * 8)[0]);
+  DA_STAMP(45, tid == 0);
   float den = 0.f;
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc[j] = 0.f;
@@ -964,6 +1008,7 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
 #pragma unroll
   for (int j = 0; j < 8; ++j) x[j] = (t_row < b) ? acc[j] * inv : 0.f;
   store_out8(out_row, x);
+  DA_STAMP(46, tid == 0);
 }
 
 // ---------------------------------------------------------------------------------
