@@ -53,6 +53,9 @@ def parse():
     ap.add_argument("--phases", action="store_true",
                     help="instead of the headline line: phase timestamps of cold calls (measurement build with "
                          "DA_PHASE_TRACE), one line per workload")
+    ap.add_argument("--ceiling", action="store_true",
+                    help="instead of the headline line: the attention against the page-stream probe, which reads "
+                         "the same tiles with the same grid and does no arithmetic (interleaved, cold)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=10.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -436,6 +439,86 @@ def mixed_lengths(args):
         torch.cuda.empty_cache()
 
 
+PROBE_MODES = {0: "LDS DMA, non-temporal (the attention's load path)", 1: "LDS DMA, default cache policy",
+               2: "register loads, non-temporal, two pages in flight per wave",
+               3: "contiguous read of the same byte count from the pool (no page table)"}
+
+
+def ceiling(args):
+    """The attention's time against the cost of its own access pattern: the page-stream
+    probe (libpage_stream_probe.so) reads the same K/V tiles of the same workload with the
+    attention's grid, LDS footprint and page-to-wave mapping and does no arithmetic
+    (modes above).  Interleaved rounds, cold (1 GiB read before every call), one event
+    pair per call; one JSON line."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    import drafter_synth as ds
+    from speculative_decoding_drafter_amd import build, drafter_attn, drafter_attn_qknorm, make_workspace, plan
+
+    lib = ctypes.CDLL(build.LIB_PROBE)
+    probe = lib.page_stream_probe
+    probe.restype = ctypes.c_int
+    probe.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
+                      ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                      ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    dev = torch.device("cuda:0")
+    case = ds.make_config(args.config)
+    g = ds.to_device(case, dev)
+    assert case.stride > 0 and g.k_pool.stride(0) == g.v_pool.stride(0) and g.k_pool.stride(1) == 64 * 64
+    S, Ps = plan(case.R, case.Hkv, case.stride)
+    ws = make_workspace(case.R, case.T, case.Hq, case.Hkv, case.stride, dev)
+    out = torch.empty(case.R * case.T, case.Hq * 64, dtype=torch.bfloat16, device=dev)
+    words = torch.zeros(case.R * case.Hkv * S * 8, dtype=torch.int32, device=dev)
+    kv = case.kv_bytes()
+    kw = dict(num_q_heads=case.Hq, num_kv_heads=case.Hkv, tokens_per_block=case.T, scale=case.scale, out=out,
+              workspace=ws)
+
+    def attention():
+        if case.qknorm:
+            drafter_attn_qknorm(g.qkv, g.k_pool, g.v_pool, g.page_table, g.context_lens, g.positions,
+                                g.q_norm_weight, g.k_norm_weight, **kw)
+        else:
+            drafter_attn(g.qkv, g.k_pool, g.v_pool, g.page_table, g.context_lens, **kw)
+
+    def run_probe(mode):
+        rc = probe(mode, g.k_pool.data_ptr(), g.v_pool.data_ptr(), g.k_pool.shape[0], 2 * g.k_pool.stride(0),
+                   case.Hkv, g.page_table.data_ptr(), case.stride, g.context_lens.data_ptr(), case.R, S, Ps, kv,
+                   words.data_ptr(), words.numel(), torch.cuda.current_stream().cuda_stream)
+        assert rc == 0, rc
+
+    variants = {"attention": attention}
+    variants.update({f"probe{m}": (lambda m=m: run_probe(m)) for m in PROBE_MODES})
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    flush_out = torch.empty((), dtype=torch.float32, device=dev)
+    res = {k: [] for k in variants}
+    rounds = max(2, args.steps // 25)
+    for rnd in range(rounds + 1):                 # round 0 is warm-up
+        for k in (list(variants) if rnd % 2 else list(variants)[::-1]):
+            evs = []
+            for _ in range(25):
+                torch.sum(flush, dim=0, out=flush_out)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(); variants[k](); e1.record()
+                evs.append((e0, e1))
+            torch.cuda.synchronize()
+            if rnd:
+                res[k] += [a.elapsed_time(b) * 1e3 for a, b in evs]
+    mean = {k: float(np.mean(v)) for k, v in res.items()}
+    med = {k: float(np.median(v)) for k, v in res.items()}
+    line = {"metric": "attention vs the cost of its access pattern (us/call, cold, event pair per call)",
+            "workload": WORKLOADS[args.config], "kv_bytes_per_call": kv, "splits": S, "pages_per_split": Ps,
+            "attention_us": round(mean["attention"], 2), "attention_median_us": round(med["attention"], 2),
+            "probe_us": {PROBE_MODES[m]: round(mean[f"probe{m}"], 2) for m in PROBE_MODES},
+            "probe_median_us": {PROBE_MODES[m]: round(med[f"probe{m}"], 2) for m in PROBE_MODES},
+            "probe_GBs": {PROBE_MODES[m]: round(kv / (mean[f"probe{m}"] * 1e-6) / 1e9, 1) for m in PROBE_MODES},
+            "attention_over_own_pattern": round(mean["attention"] / mean["probe0"], 4),
+            "calls_each": len(res["attention"])}
+    print(json.dumps(line), flush=True)
+
+
 def phases(args):
     """Where a cold call's time goes: the phase timestamps of the measurement build
     (DA_PHASE_TRACE; per workgroup, see the kernel source), for the four configurations and
@@ -544,6 +627,9 @@ def main():
         return
     if args.phases:
         phases(args)
+        return
+    if args.ceiling:
+        ceiling(args)
         return
     import torch
 

@@ -7,11 +7,11 @@ What is computed (TensorRT-LLM PR #20532 "Share Kimi K3 FP4 modeling and add
 NVFP4 support on SM103", Conversation, the commit that adds k3_drafter_attn
 and k3_drafter_attn_qknorm, and the next commit that adds their contracts):
 
-* Up to 8 requests each bring a draft block of up to 8 tokens.  Every block
-  attends densely -- no causal mask -- to its request's paged context and to
-  its own K/V, which come from the packed qkv rows and are never written to
-  the page pool.
-* GQA with 6 query heads per KV head, head_dim 64, HND pages of 64 tokens.
+* batch: R <= 8 requests, T <= 8 block tokens per request.
+* keys of request r: its context tokens (HND pages of 64 through its
+  page-table row), then its block tokens' k/v columns of the packed qkv rows;
+  no mask; the pool is only read.
+* heads: GQA, 6 query heads per KV head, head_dim 64.
 * k3_drafter_attn takes q/k already normalised and rotated;
   k3_drafter_attn_qknorm applies the per-head q/k RMSNorm (eps 1e-5) and the
   NeoX rotary embedding (base 10000) itself.

@@ -29,21 +29,24 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build the HIP library)")
 
 
-# Measurement builds of the same source, loaded only by bench.py: the static split
+# Measurement builds, loaded only by bench.py: the same source with the static split
 # plan alone (the reference `bench.py --mixed` measures the length-aware schedule
-# against) and the kernels with phase timestamps (`bench.py --phases`).
+# against) and with phase timestamps (`bench.py --phases`); and the page-stream probe,
+# the attention's context reads without the attention (`bench.py --ceiling`).
 LIB_STATIC_PLAN = os.path.join(PKG, "libdrafter_attn_static_plan.so")
 LIB_PHASES = os.path.join(PKG, "libdrafter_attn_phases.so")
-VARIANTS = {None: (LIB, []), "static_plan": (LIB_STATIC_PLAN, ["-DDA_STATIC_PLAN_ONLY"]),
-            "phases": (LIB_PHASES, ["-DDA_PHASE_TRACE"])}
+LIB_PROBE = os.path.join(PKG, "libpage_stream_probe.so")
+PROBE_SRC = os.path.join(PKG, "csrc", "page_stream_probe.hip")
+VARIANTS = {None: (LIB, [], SRC), "static_plan": (LIB_STATIC_PLAN, ["-DDA_STATIC_PLAN_ONLY"], SRC),
+            "phases": (LIB_PHASES, ["-DDA_PHASE_TRACE"], SRC), "probe": (LIB_PROBE, [], PROBE_SRC)}
 
 
 def build_library(verbose: bool = False, variant: str = None) -> str:
-    """Compile the library (or a measurement build of it) from source, always, and
-    return the path of the .so."""
-    lib, extra = VARIANTS[variant]
+    """Compile the library (or a measurement build) from source, always, and return
+    the path of the .so."""
+    lib, extra, src = VARIANTS[variant]
     tmp = lib + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, *extra, "-I", INCLUDE, "-o", tmp, SRC]
+    cmd = [hipcc(), *HIPCC_FLAGS, *extra, "-I", INCLUDE, "-o", tmp, src]
     res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     msgs = [ln for ln in res.stdout.splitlines() if "packed-fp32-ops" not in ln]
     if res.returncode != 0:

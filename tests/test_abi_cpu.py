@@ -363,3 +363,38 @@ def test_noalloc_scratch_limit_in_partial_slots(lib):
         assert rc == DA_EWORKSPACE and "scratch" in _lib.last_error(), (R, hkv, stride, n)
         refused += 1
     assert refused >= 3
+
+
+# ---- the page-stream probe (measurement library of bench.py --ceiling): loads, exports its
+# entry point and refuses arguments that do not fit before any device call
+
+@pytest.fixture(scope="module")
+def probe_lib():
+    from speculative_decoding_drafter_amd import build
+    if not os.path.exists(build.LIB_PROBE):
+        pytest.skip("probe library not built")
+    lib = ctypes.CDLL(build.LIB_PROBE)
+    fn = lib.page_stream_probe
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
+                   ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                   ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    return fn
+
+
+PROBE_OK = dict(mode=0, k=0x1000, v=0x2000, num_pages=5000, page_bytes=65536, Hkv=4, pt=0x3000, stride=512,
+                lens=0x4000, R=8, S=8, Ps=64, stream=268435456, out=0x5000, out_words=2048, hip_stream=None)
+
+
+@pytest.mark.parametrize("over", [
+    dict(mode=4), dict(mode=-1), dict(k=None), dict(v=None), dict(pt=None), dict(lens=None), dict(out=None),
+    dict(R=0), dict(Hkv=0), dict(S=0), dict(Ps=0), dict(Ps=513), dict(stride=0),
+    dict(S=7),                      # 7 splits of 64 pages do not cover a 512-page row
+    dict(num_pages=0), dict(out_words=2047),
+    dict(page_bytes=32768 - 16), dict(page_bytes=65536 + 8), dict(page_bytes=(1 << 32) + 16),
+    dict(mode=3, stream=8), dict(mode=3, stream=268435456 + 4), dict(mode=3, stream=4999 * 65536 + 32768 + 16),
+])
+def test_probe_refuses_arguments_that_do_not_fit(probe_lib, over):
+    a = dict(PROBE_OK, **over)
+    assert probe_lib(a["mode"], a["k"], a["v"], a["num_pages"], a["page_bytes"], a["Hkv"], a["pt"], a["stride"],
+                     a["lens"], a["R"], a["S"], a["Ps"], a["stream"], a["out"], a["out_words"], a["hip_stream"]) == -1

@@ -107,8 +107,11 @@ def _m0_outside_asm(asm: str):
     return inside, outside, bad_blocks
 
 
-@pytest.fixture(scope="module")
-def device_asm(tmp_path_factory):
+PROBE_SRC = os.path.join(os.path.dirname(SRC), "page_stream_probe.hip")
+
+
+@pytest.fixture(scope="module", params=[SRC, PROBE_SRC], ids=["attention", "page_stream_probe"])
+def device_asm(request, tmp_path_factory):
     import shutil
     import subprocess
 
@@ -116,10 +119,10 @@ def device_asm(tmp_path_factory):
     if not os.path.exists(hipcc):
         pytest.skip("hipcc not available")
     inc = os.path.join(os.path.dirname(os.path.dirname(SRC)), "..", "include")
-    out = tmp_path_factory.mktemp("asm") / "drafter.s"
+    out = tmp_path_factory.mktemp("asm") / "device.s"
     cmd = [hipcc, "-O3", "-std=c++17", "--offload-arch=gfx950", "--cuda-device-only", "-S",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-I", os.path.abspath(inc), "-o", str(out),
-           SRC]
+           request.param]
     res = subprocess.run(cmd, capture_output=True, text=True, timeout=300)
     assert res.returncode == 0, res.stderr
     return out.read_text()
