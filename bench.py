@@ -587,10 +587,10 @@ def phases(args):
             pos = lambda a: a[a > 0]
             ends = d[:, 46]
             last = int(np.argmax(ends))
-            early = d[:, 22:24][d[:, 22:24] > 0]  # waves 6-7 issue their first page before the prologue
+            early = pos(d[:, 48:56])  # waves that issue their first page before the prologue
             row = {"prologue_loads_landed": np.median(us(pos(d[:, 8:16]))),
-                   "first_dma_issued_waves_6_7": np.median(us(early)) if early.size else float("nan"),
-                   "first_dma_issued_all_waves": np.median(us(pos(d[:, 16:24]))),
+                   "first_dma_issued_early_waves": np.median(us(early)) if early.size else float("nan"),
+                   "prologue_done_first_dma_issued_all_waves": np.median(us(pos(d[:, 16:24]))),
                    "prologue_barrier": np.median(us(pos(d[:, 47]))),
                    "first_k_tile_landed": np.median(us(pos(d[:, 24:32]))),
                    "loop_end_median": np.median(us(pos(d[:, 32:40]))),
@@ -598,7 +598,7 @@ def phases(args):
                    "end": us(ends[last])}
             for k, name in ((41, "last_group_merge_barrier"), (42, "last_group_merged"),
                             (43, "last_group_published"), (44, "last_group_counter"),
-                            (45, "last_group_combine_weights")):
+                            (45, "last_group_combine_loads_landed")):
                 row[name] = us(d[last, k]) if d[last, k] > 0 else float("nan")
             stats.append(row)
         med = {k: round(float(np.median([r[k] for r in stats])), 2) for k in stats[0]}

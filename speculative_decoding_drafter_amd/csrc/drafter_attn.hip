@@ -437,11 +437,13 @@ __device__ __forceinline__ void attend_page(const unsigned char* kt, const unsig
 // Phase timestamps for measurement builds (DA_PHASE_TRACE defined; the product build
 // compiles them out): 64 u64 slots per workgroup, at (uint64_t*)status_word + 64 * the
 // workgroup's linear index, each a reading of the 100 MHz real-time counter:
-//   [w] wave w starts, [8+w] its prologue loads have landed, [16+w] it has issued its
-//   first page's DMA, [24+w] that page's K tile has landed, [32+w] its page loop ends,
-//   [40] XCC id, [41] after the merge barrier, [42] merged, [43] partial published,
-//   [44] counter taken, [45] combine weights done, [46] output stored, [47] after the
-//   prologue barrier.  The status flags are off in such builds.
+//   [w] wave w starts, [8+w] its prologue loads have landed, [16+w] its share of the
+//   prologue is done and its first page's DMA issued, [24+w] that page's K tile has
+//   landed, [32+w] its page loop ends, [40] XCC id, [41] after the merge barrier, [42]
+//   merged, [43] partial published, [44] counter taken, [45] the combine's loads have
+//   landed (with more than 8 splits: every chunk merged), [46] output stored, [47] after the prologue
+//   barrier, [48+w] a wave that issues its first page before the prologue has issued it.
+//   The status flags are off in such builds.
 #ifdef DA_PHASE_TRACE
 #define DA_STAMP(slot, cond)                                                              \
   do {                                                                                   \
@@ -649,6 +651,7 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
     stage_tile<false>(p.kpool + page_off(0), lds_k, doff);
     stage_tile<true>(p.vpool + page_off(0), lds_v, doff);
   }
+  DA_STAMP(48 + w, lane == 0 && early_dma && cnt > 0);
 
   // ---- length-aware split scheduling (BAL), decided while the first pages are in
   // flight.  Every workgroup derives the same schedule from the lengths (device data)
@@ -964,32 +967,28 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
   const __amdgpu_buffer_rsrc_t pm = dev_rsrc(p.part_ml + static_cast<int64_t>(slot0) * kRows * 2, S * kRows * 2 * 4);
   const __amdgpu_buffer_rsrc_t po = dev_rsrc(p.part_o + static_cast<int64_t>(slot0) * kRows * kD, S * kRows * kD * 4);
   constexpr int kChunk = 8;
-  f32x2 ml[kChunk];
-  f32x4 ov[kChunk][2];
-  auto load_chunk = [&](int s0) {
+  float den = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = 0.f;
+  if (S <= kChunk) {
+    // one chunk: the maximum over all splits first, then the weighted sums
+    f32x2 ml[kChunk];
+    f32x4 ov[kChunk][2];
 #pragma unroll
     for (int j = 0; j < kChunk; ++j) {
       ml[j] = f32x2{-INFINITY, 0.f};
       ov[j][0] = ov[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (s0 + j < S) {
-        const int prow = (s0 + j) * kRows + row;
+      if (j < S) {
+        const int prow = j * kRows + row;
         ml[j] = ld_dev_b64(pm, prow * 8);
         ov[j][0] = ld_dev_b128(po, (prow * kD + 4 * oc) * 4);
         ov[j][1] = ld_dev_b128(po, (prow * kD + 4 * oc) * 4 + 128);
       }
     }
-  };
-  load_chunk(0);
-  float m_all = -INFINITY;
+    float m_all = -INFINITY;
 #pragma unroll
-  for (int j = 0; j < kChunk; ++j) m_all = fmaxf(m_all, ml[j][0]);
-  for (int k = kChunk; k < S; ++k) m_all = fmaxf(m_all, ld_dev_b64(pm, (k * kRows + row) * 8)[0]);
-  DA_STAMP(45, tid == 0);
-  float den = 0.f;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) acc[j] = 0.f;
-  for (int s0 = 0; s0 < S; s0 += kChunk) {
-    if (s0 > 0) load_chunk(s0);
+    for (int j = 0; j < kChunk; ++j) m_all = fmaxf(m_all, ml[j][0]);
+    DA_STAMP(45, tid == 0);
 #pragma unroll
     for (int j = 0; j < kChunk; ++j) {
       // split weight exp2(c (m_s - M)); a split that saw no key (m = -inf) has weight 0
@@ -1001,6 +1000,48 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
         acc[4 + q] = fmaf(e, ov[j][1][q], acc[4 + q]);
       }
     }
+  } else {
+    // More splits (up to 64): chunks of 8 in split order, each loaded whole (one round
+    // trip) and merged with a running maximum -- when a chunk raises it, what has been
+    // summed so far is rescaled.  The loads are unconditional: past the last split the
+    // buffer's range check returns zeros, which the mask gives weight 0.
+    f32x2 ml[kChunk];
+    f32x4 ov[kChunk][2];
+    float m_run_all = -INFINITY;
+    for (int s0 = 0; s0 < S; s0 += kChunk) {
+#pragma unroll
+      for (int j = 0; j < kChunk; ++j) {
+        const int prow = (s0 + j) * kRows + row;
+        ml[j] = ld_dev_b64(pm, prow * 8);
+        ov[j][0] = ld_dev_b128(po, (prow * kD + 4 * oc) * 4);
+        ov[j][1] = ld_dev_b128(po, (prow * kD + 4 * oc) * 4 + 128);
+      }
+      float mj[kChunk];
+      float mc = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < kChunk; ++j) {
+        mj[j] = s0 + j < S ? ml[j][0] : -INFINITY;
+        mc = fmaxf(mc, mj[j]);
+      }
+      const float mn = fmaxf(m_run_all, mc);
+      // nothing summed yet (running maximum -inf): the sums are zero, scale 0
+      const float sc = (m_run_all == -INFINITY) ? 0.f : fast_exp2((m_run_all - mn) * p.c);
+      den *= sc;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[q] *= sc;
+#pragma unroll
+      for (int j = 0; j < kChunk; ++j) {
+        const float e = (mj[j] == -INFINITY) ? 0.f : fast_exp2((mj[j] - mn) * p.c);
+        den = fmaf(ml[j][1], e, den);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc[q] = fmaf(e, ov[j][0][q], acc[q]);
+          acc[4 + q] = fmaf(e, ov[j][1][q], acc[4 + q]);
+        }
+      }
+      m_run_all = mn;
+    }
+    DA_STAMP(45, tid == 0);
   }
   // den > 0 whenever there is a key (always with the block's own keys, in split 0)
   const float inv = den > 0.f ? 1.0f / den : 0.f;
