@@ -116,3 +116,22 @@ def test_traffic_record_key_follows_device_code_and_plan(tmp_path, monkeypatch):
     assert device_edit != src and hash_of(device_edit) != base
     plan_edit = src.replace("kTargetWorkgroups = 256", "kTargetWorkgroups = 512")
     assert plan_edit != src and hash_of(plan_edit) != base
+
+
+def test_balanced_plan_of_the_mixed_workloads():
+    # the plan bench.py --mixed reports for each of its workloads, by the documented rule
+    # (Pb = smallest multiple of 8 >= ceil(N / (R (S-1))) and >= ceil(max npg / 32), taken
+    # only when Pb <= 3/4 of the static split rounded down to a multiple of 8)
+    sys.path.insert(0, ROOT)
+    import bench
+
+    want = [(True, 32), (True, 64), (True, 32), (True, 8), (False, 64), (False, 64)]
+    got = []
+    for _, R, Hq, Hkv, stride, lens in bench.MIXED:
+        if isinstance(lens, tuple):
+            lens = [int(x) for x in np.random.default_rng(lens[0]).integers(0, lens[1] + 1, R)]
+        got.append(bench.balanced_plan(R, Hkv, stride, lens))
+    assert got == want
+    # equal lengths never balance; one long request among empty ones always does when there is room
+    assert bench.balanced_plan(8, 4, 512, [32768] * 8) == (False, 64)
+    assert bench.balanced_plan(8, 4, 1024, [65536] + [0] * 7)[0]
