@@ -46,7 +46,7 @@ def parse():
                          "call; reported beside the headline, not instead of it")
     ap.add_argument("--large", action="store_true",
                     help="instead of the headline line: one line per large context (131k and 1M tokens, "
-                         "24/4 and 96/16 heads), pools drawn on the device")
+                         "24/4 and 96/16 heads; one request of 32k and 131k tokens), pools drawn on the device")
     ap.add_argument("--mixed", action="store_true",
                     help="instead of the headline line: the length-aware split schedule against the static plan "
                          "alone, on mixed-length workloads (one line per workload)")
@@ -200,19 +200,23 @@ def write_traffic(fetch_csv: str, write_csv: str, workload: int, dest: str = Non
     return rec
 
 
-LARGE = [(8, 24, 4, 2048), (8, 24, 4, 16384), (8, 96, 16, 16384)]  # R, Hq, Hkv, pages per request
+LARGE = [(8, 24, 4, 2048), (8, 24, 4, 16384), (8, 96, 16, 16384),  # R, Hq, Hkv, pages per request
+         (1, 24, 4, 512), (1, 24, 4, 2048)]                           # one request: 32k and 131k tokens
 
 
 def large_contexts(args):
     """Context lengths beyond the headline workload (8 x 8 tokens, qknorm, every request at the
-    same length): 131k tokens at 24/4 heads, 1M tokens at 24/4 and at 96/16 heads.  The pools
-    (1.1 to 34 GB, all larger than the 256 MB Infinity Cache) are drawn on the device; one JSON
-    line per size, mean of event-timed calls after warm-up."""
+    same length): 131k tokens at 24/4 heads, 1M tokens at 24/4 and at 96/16 heads; and one
+    request of 32k and of 131k tokens at 24/4 heads (plans of 64 splits).  The pools (67 MB to
+    34 GB) are drawn on the device; one JSON line per size, mean of event-timed calls after
+    warm-up, each after the untimed 1 GiB read (cold caches)."""
     import torch
 
     import drafter_synth as ds
-    from speculative_decoding_drafter_amd import drafter_attn_qknorm, make_workspace
+    from speculative_decoding_drafter_amd import drafter_attn_qknorm, make_workspace, plan
 
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    flush_out = torch.empty((), dtype=torch.float32, device="cuda")
     for R, Hq, Hkv, pages in LARGE:
         pool = ds.device_normal_pool(R * pages, Hkv, seed=5, device="cuda")
         case = ds.make_case(R, 8, Hq, Hkv, [pages * 64] * R, seed=5, stride=pages, pool_pages=R * pages,
@@ -228,12 +232,14 @@ def large_contexts(args):
         for _ in range(args.warmup // 4 + 1):
             call()
         torch.cuda.synchronize()
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(max(5, args.steps // 20))]
-        for a, b in evs:
+        evs = []
+        for _ in range(max(5, args.steps // 20)):
+            torch.sum(flush, dim=0, out=flush_out)  # cold: the one-request pools fit the Infinity Cache
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
             call()
             b.record()
+            evs.append((a, b))
         torch.cuda.synchronize()
         ms = sum(a.elapsed_time(b) for a, b in evs) / len(evs)
         kv = R * pages * Hkv * 2 * 64 * 64 * 2
@@ -241,6 +247,7 @@ def large_contexts(args):
                           "q_heads": Hq, "kv_heads": Hkv, "context_tokens": pages * 64, "kv_bytes_per_call": kv,
                           "us_per_call": round(ms * 1e3, 1), "GBs": round(kv / (ms * 1e-3) / 1e9, 1),
                           "pct_of_hbm_peak": round(100 * kv / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 1),
+                          "splits": plan(R, Hkv, pages)[0], "cache": "cold (1 GiB read before each call)",
                           "calls_timed": len(evs)}), flush=True)
         del pool, case, g, ws, out
         torch.cuda.empty_cache()
@@ -748,10 +755,10 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "traffic": None if args.hot else measured_traffic(args.config),
-                     "kernel": "drafter_attn_kernel<%d,%s,%s,true,%s>" % (
+                     "kernel": "drafter_attn_kernel<%d,%s,%s,true,%s,%s>" % (
                          (6 * case.T + 15) // 16, str(case.qknorm).lower(),
                          str(case.qknorm and case.positions.dtype == torch.int64).lower(),
-                         str(S > 1 and Ps >= 32).lower())},
+                         str(S > 1 and Ps >= 32).lower(), str(S > 16).lower())},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(case, args.cpu_budget_s)

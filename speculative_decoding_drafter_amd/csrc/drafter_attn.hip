@@ -52,6 +52,7 @@ constexpr int kMaxSplits = 64;
 constexpr int kMaxStride = 16384;            // pages per request row (with 64 splits: <= 256 per split)
 constexpr int kMaxPagesPerSplit = 64 * kWaves;  // a wave's page ids fit one 64-lane VGPR
 constexpr int kMaxReqSplits = 32;             // balanced plan: splits per request (bounds its combine)
+constexpr int kTwoLevel = 16;                 // plans with more splits combine a request in two levels
 constexpr int kTileBytes = kPage * kD * 2;   // one [64][64] bf16 tile, 8 KiB
 constexpr int kStageBytes = 2 * kTileBytes;  // a wave's K slot then V slot
 constexpr float kRescaleLog2 = 8.0f;         // lazy-rescale headroom (exp2 units)
@@ -112,7 +113,7 @@ struct Params {
   const uint16_t* wk;
   float* part_o;     // [R*Hkv*S][48][64]
   float* part_ml;    // [R*Hkv*S][48][2]
-  uint32_t* counters;  // [R*Hkv][kCounterStride], word 0 of each used
+  uint32_t* counters;  // [R*Hkv][kCounterStride]: word 0, and 1..8 for two-level combines
   uint16_t* out;
   int64_t out_stride;
   int32_t* status;
@@ -547,7 +548,7 @@ __device__ __forceinline__ u32x4 pack8(const float (&x)[8]) {
 // OWN = false is the attention of the path the fused op replaces: the block's
 // queries attend to pooled keys only (the caller appended the block to the pool and
 // passes kv lengths L + b), nothing is read from qkv but the queries.
-template <int NT, bool QKNORM, bool POS64, bool OWN = true, bool BAL = false>
+template <int NT, bool QKNORM, bool POS64, bool OWN = true, bool BAL = false, bool MANY = false>
 __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kSmemBytes];
   int s = blockIdx.x, r = blockIdx.z;
@@ -947,6 +948,102 @@ __global__ __launch_bounds__(kThreads) void drafter_attn_kernel(const Params p) 
   wait_vmcnt<0>();  // this thread's partial stores are complete (visible at device scope)
   __syncthreads();
   DA_STAMP(43, tid == 0);
+  if constexpr (MANY) {
+    // A request with more than kTwoLevel splits (plans of more than kTwoLevel splits
+    // only: the kernel of the other plans is compiled without this) merges in two
+    // levels: the last workgroup of each group of 8 consecutive splits merges its group
+    // into the group's first slot (whose partial it has just read back) and publishes
+    // it, and the last of the groups merges the groups, in group order -- the partials'
+    // loads spread over several CUs instead of one CU reading them all, chunk by chunk.
+    if (s_used > kTwoLevel) {
+      const int grp = s >> 3;
+      const int ngrp = (s_used + 7) >> 3;
+      uint32_t* ctr = p.counters + kCounterStride * rg;
+      int* flag2 = reinterpret_cast<int*>(smem + kOffFlag);
+      if (tid == 0) {
+        const int n = min(8, s_used - 8 * grp);
+        const uint32_t prev = __hip_atomic_fetch_add(ctr + 1 + grp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int is_last = (prev == static_cast<uint32_t>(n - 1));
+        if (is_last) __hip_atomic_store(ctr + 1 + grp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *flag2 = is_last;
+      }
+      __syncthreads();
+      DA_STAMP(44, tid == 0);
+      if (!*flag2) return;
+      float sum[8], den2 = 0.f;
+      // n <= 8 partials at slots base + stride * j into (maximum, den2, sum)
+      auto merge8 = [&](int base, int stride, int n) {
+        den2 = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) sum[j] = 0.f;
+        const int extent = (n - 1) * stride + 1;
+        const __amdgpu_buffer_rsrc_t pm =
+            dev_rsrc(p.part_ml + static_cast<int64_t>(base) * kRows * 2, extent * kRows * 2 * 4);
+        const __amdgpu_buffer_rsrc_t po =
+            dev_rsrc(p.part_o + static_cast<int64_t>(base) * kRows * kD, extent * kRows * kD * 4);
+        f32x2 ml[8];
+        f32x4 ov[8][2];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          ml[j] = f32x2{-INFINITY, 0.f};
+          ov[j][0] = ov[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+          if (j < n) {
+            const int prow = j * stride * kRows + row;
+            ml[j] = ld_dev_b64(pm, prow * 8);
+            ov[j][0] = ld_dev_b128(po, (prow * kD + 4 * oc) * 4);
+            ov[j][1] = ld_dev_b128(po, (prow * kD + 4 * oc) * 4 + 128);
+          }
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) mx = fmaxf(mx, ml[j][0]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float e = (ml[j][0] == -INFINITY) ? 0.f : fast_exp2((ml[j][0] - mx) * p.c);
+          den2 = fmaf(ml[j][1], e, den2);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            sum[q] = fmaf(e, ov[j][0][q], sum[q]);
+            sum[4 + q] = fmaf(e, ov[j][1][q], sum[4 + q]);
+          }
+        }
+        return mx;
+      };
+      // level 1: the group's partials, published as the group's partial in its first slot
+      const int gbase = slot0 + 8 * grp;
+      if (row_thread) {
+        const float m_g = merge8(gbase, 1, min(8, s_used - 8 * grp));
+        const __amdgpu_buffer_rsrc_t po = dev_rsrc(p.part_o + static_cast<int64_t>(gbase) * kRows * kD, kRows * kD * 4);
+        const int off = (row * kD + 4 * oc) * 4;
+        st_dev_b128(po, off, f32x4{sum[0], sum[1], sum[2], sum[3]});
+        st_dev_b128(po, off + 128, f32x4{sum[4], sum[5], sum[6], sum[7]});
+        if (oc == 0) {
+          const __amdgpu_buffer_rsrc_t pm = dev_rsrc(p.part_ml + static_cast<int64_t>(gbase) * kRows * 2, kRows * 2 * 4);
+          st_dev_b64(pm, row * 8, f32x2{m_g, den2});
+        }
+      }
+      wait_vmcnt<0>();  // the group's partial is complete (visible at device scope)
+      __syncthreads();  // every thread has read the group's flag
+      if (tid == 0) {
+        const uint32_t prev = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int is_last = (prev == static_cast<uint32_t>(ngrp - 1));
+        if (is_last) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *flag2 = is_last;
+      }
+      __syncthreads();
+      if (!*flag2 || !row_thread) return;
+      // level 2: the groups' partials, in group order
+      merge8(slot0, 8, ngrp);
+      DA_STAMP(45, tid == 0);
+      const float inv = den2 > 0.f ? 1.0f / den2 : 0.f;
+      float x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = (t_row < b) ? sum[j] * inv : 0.f;
+      store_out8(out_row, x);
+      DA_STAMP(46, tid == 0);
+      return;
+    }
+  }
   int* last = reinterpret_cast<int*>(smem + kOffFlag);
   if (tid == 0) {
     uint32_t* ctr = p.counters + kCounterStride * rg;
@@ -1366,12 +1463,22 @@ Params make_params(const Common& a, const Plan& plan, const WsLayout& l) {
 template <int NT, bool QK, bool P64, bool OWN>
 int launch_t(const Params& p, const Plan& plan, hipStream_t stream) {
   dim3 grid(plan.S, p.Hkv, p.R);
-  // the length-aware schedule is compiled in only where the plan leaves it room: its
-  // code costs the static path 0.4 us even where it is never taken
-  if (p.bal_n > 0)
-    hipLaunchKernelGGL((drafter_attn_kernel<NT, QK, P64, OWN, true>), grid, dim3(kThreads), 0, stream, p);
-  else
-    hipLaunchKernelGGL((drafter_attn_kernel<NT, QK, P64, OWN, false>), grid, dim3(kThreads), 0, stream, p);
+  // The length-aware schedule is compiled in only where the plan leaves it room (its
+  // code costs the static path 0.1-0.8 us on the 32k workload even where it is never
+  // taken), and the two-level combine only into the kernel of plans with more than
+  // kTwoLevel splits (its code moves the page loop's scheduling: +0.1-0.25 us elsewhere).
+  const bool many = plan.S > kTwoLevel;
+  if (p.bal_n > 0) {
+    if (many)
+      hipLaunchKernelGGL((drafter_attn_kernel<NT, QK, P64, OWN, true, true>), grid, dim3(kThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL((drafter_attn_kernel<NT, QK, P64, OWN, true, false>), grid, dim3(kThreads), 0, stream, p);
+  } else {
+    if (many)
+      hipLaunchKernelGGL((drafter_attn_kernel<NT, QK, P64, OWN, false, true>), grid, dim3(kThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL((drafter_attn_kernel<NT, QK, P64, OWN, false, false>), grid, dim3(kThreads), 0, stream, p);
+  }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(DA_ELAUNCH, std::string("launch failed: ") + hipGetErrorString(e));
   return DA_OK;
