@@ -106,8 +106,8 @@ enum {
  * Bytes of workspace a call with these sizes needs (0 for arguments outside the
  * contract, a head_dim other than 64 included).  The workspace holds one fp32
  * partial (running max, weight sum, unnormalised output) per (request, KV head,
- * context split) and one counter per (request, KV head), each counter on its own
- * 256-byte line.  The workspace must be 256-byte aligned (as hipMalloc returns).
+ * context split) and one 256-byte line of arrival counters per (request, KV head)
+ * (word 0; words 1..8 too where a request's splits are combined in two levels).  The workspace must be 256-byte aligned (as hipMalloc returns).
  * The counters must be zero before the first call on a workspace (zero the whole
  * buffer once after allocating it); every call leaves them zero again.  Two calls
  * in flight on one workspace race.
