@@ -19,10 +19,15 @@
 //      partial per workgroup;
 //   4. the last workgroup of each (r, g) (device-scope counter, reset by that
 //      workgroup) merges the splits in fixed order and writes bf16 output; a
-//      request that fits one split writes its output from that split directly.
+//      request that fits one split writes its output from that split directly,
+//      and under a plan of more than 16 splits a request using more than 16
+//      merges in two levels (groups of 8 splits, then the groups).
+// Where the plan leaves room, the kernel also reads every request's length and
+// may take a balanced split schedule (decided on the device from the lengths).
 // Nothing depends on device data except through loads, so the same launch is
 // valid for any rewritten lengths / page tables / qkv (graph replay), and the
-// split plan and every reduction order are fixed (bit-identical reruns).
+// split plan and every reduction order follow from the sizes and the lengths
+// alone (bit-identical reruns).
 //
 // Also here: the standalone in-place q/k RMSNorm + NeoX rotation (the same
 // per-row arithmetic as the attention prologue), and, as a baseline for the
