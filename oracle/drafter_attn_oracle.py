@@ -377,7 +377,7 @@ def drafter_attn_split_merge(qkv, k_pool, v_pool, page_table, context_lens, bloc
                              tokens_per_block: int, scale: Optional[float] = None,
                              positions=None, q_norm_weight=None, k_norm_weight=None,
                              eps: float = 1e-5, rope_base: float = 10000.0,
-                             qknorm: bool = False, **_unused):
+                             qknorm: bool = False, group: Optional[int] = None, **_unused):
     """The same attention computed split-KV (flash-decoding) style.
 
     The context pages of a request are cut into ``num_splits`` consecutive page
@@ -385,7 +385,10 @@ def drafter_attn_split_merge(qkv, k_pool, v_pool, page_table, context_lens, bloc
     maximum ``m``, weight sum ``l`` and unnormalised output ``O``; the ranges
     are merged by rescaling with ``exp(m_s - M)``, ``M = max_s m_s``.  This is
     the algebra of the split-combine pass, checked here against the plain
-    definition independently of any GPU code.
+    definition independently of any GPU code.  With ``group`` the context
+    ranges are first merged in consecutive groups of that many, each group
+    giving one (m, l, O) of the same form, and the groups are merged after
+    (a two-level combine: the merge is associative).
     """
     if scale is None:
         scale = 1.0 / math.sqrt(HEAD_DIM)
@@ -424,12 +427,23 @@ def drafter_attn_split_merge(qkv, k_pool, v_pool, page_table, context_lens, bloc
                 m = s.max(axis=-1)
                 e = np.exp(s - m[:, None])
                 parts.append((m, e.sum(axis=-1), e @ vv))
-            M = np.max([p[0] for p in parts], axis=0)
-            num = np.zeros((b, D))
-            den = np.zeros(b)
-            for m, l, o in parts:
-                w = np.where(np.isfinite(m), np.exp(m - M), 0.0)
-                num += w[:, None] * o
-                den += w * l
+            if group:
+                ctx = parts[:num_splits]  # the context ranges; the own block stays a range of its own
+                parts = [_merge_parts(ctx[i:i + group], b, D) for i in range(0, num_splits, group)] + parts[num_splits:]
+            m_all, den, num = _merge_parts(parts, b, D)
             out[rows, h * D:(h + 1) * D] = num / den[:, None]
     return out
+
+
+def _merge_parts(parts, b: int, D: int):
+    """Merge (m, l, O) range results into one of the same form: ``M = max m``,
+    ``l = sum l exp(m - M)``, ``O = sum O exp(m - M)`` (a range without keys has
+    ``m = -inf`` and weight 0)."""
+    M = np.max([p[0] for p in parts], axis=0)
+    num = np.zeros((b, D))
+    den = np.zeros(b)
+    for m, l, o in parts:
+        w = np.where(np.isfinite(m), np.exp(m - np.where(np.isfinite(M), M, 0.0)), 0.0)
+        num += w[:, None] * o
+        den += w * l
+    return M, den, num

@@ -22,6 +22,18 @@ orig_attend = mod._softmax_attend
 orig_qknr = mod.qk_norm_rope
 orig_append = mod.kv_append
 orig_paged = mod.paged_attn
+orig_merge = mod._merge_parts
+
+
+def _merge_no_rescale(parts, b, D):
+    # every range weighted 1 instead of exp(m - M)
+    return orig_merge([(np.where(np.isfinite(m), 0.0, m), l, o) for m, l, o in parts], b, D)
+
+
+def _merge_max_of_first(parts, b, D):
+    # the reference maximum taken from the first range only
+    M0 = parts[0][0]
+    return orig_merge([(np.minimum(m, M0) if i else m, l, o) for i, (m, l, o) in enumerate(parts)], b, D)
 
 
 def _append_next_slot(k_pool, v_pool, qkv, page_table, context_lens, block_lens=None, **kw):
@@ -185,6 +197,8 @@ MUTATIONS = {
     "yarn_multiplies_by_s": ("yarn_inv_freq", _yarn_times_s),
     "yarn_mscale_log10": ("yarn_mscale", lambda f: 0.1 * np.log10(f) + 1.0),
     "yarn_no_mscale": ("yarn_mscale", lambda f: 1.0),
+    "merge_no_rescale": ("_merge_parts", _merge_no_rescale),
+    "merge_max_of_first_range": ("_merge_parts", _merge_max_of_first),
 }
 
 
@@ -216,6 +230,15 @@ def _battery():
             pins.test_replaced_path_equals_fused_definition(i)
         except Exception:  # any error is a failed pin
             failed.append(f"replaced{i}")
+    # the split-merge algebra, flat and in two levels, on a small case
+    sm = ds.make_case(2, 3, 12, 2, [700, 130], seed=79, qknorm=True, pool_pages=14)
+    for S, G in ((3, None), (9, 4)):
+        try:
+            got = oracle.drafter_attn_split_merge(**sm.np_args(), num_splits=S, group=G, qknorm=True)
+            if not pins._rel(got, pins._oracle(sm)) <= pins.TOL:
+                failed.append(f"split_merge{S}")
+        except Exception:  # any error is a failed pin
+            failed.append(f"split_merge{S}")
     for where in ("first", "tail_slot", "block"):
         try:
             pins.test_needle(where)

@@ -128,6 +128,16 @@ def test_split_merge_equals_definition(S):
     assert _rel(got, ref) <= 1e-13
 
 
+@pytest.mark.parametrize("S,G", [(17, 8), (33, 8), (64, 8), (9, 4)])
+def test_two_level_split_merge_equals_definition(S, G):
+    # ranges merged in groups of G first, then the groups (the GPU's two-level combine);
+    # with 64 splits of a 33-page row most groups hold no key at all
+    case = ds.make_config(2)
+    ref = _oracle(case)
+    got = oracle.drafter_attn_split_merge(**case.np_args(), num_splits=S, group=G, qknorm=True)
+    assert _rel(got, ref) <= 1e-13
+
+
 def test_softmax_weights_sum_to_one():
     case = ds.make_config(3)
     _, probs = _oracle(case, return_probs=True)
