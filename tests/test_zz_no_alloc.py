@@ -44,6 +44,18 @@ def test_noalloc_matches_workspace_entry_point_twice():
         check(to_np(out_na), reference(case, pools), f"noalloc-{case.name or 'cfg5'}")
 
 
+def test_noalloc_one_long_request_two_level_combine():
+    # one 32k-token request: a plan of 64 splits, merged in two levels (counter words 1..8
+    # of the scratch's counter lines as well as word 0), twice in a row
+    case = ds.make_case(1, 8, 24, 4, [32768 - 5], seed=402, qknorm=True, name="one-long")
+    g = ds.to_device(case, "cuda")
+    for k in range(2):
+        say(f"noalloc: one long request, call {k}")
+        out_na, out_ws = _both(case, g)
+        assert torch.equal(out_na, out_ws), f"call {k}: no-allocation output differs from the workspace call"
+    check(to_np(out_na), reference(case), "noalloc-one-long")
+
+
 def test_noalloc_graph_replay_with_rewritten_inputs():
     from speculative_decoding_drafter_amd import drafter_attn_qknorm, drafter_attn_qknorm_noalloc
 
