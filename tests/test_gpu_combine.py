@@ -68,9 +68,14 @@ def test_many_split_combine(name):
     if grow is not None:
         _ramp(case, grow)
     say(f"many-split combine {name}: splits {splits}, lengths {lens}")
+    from speculative_decoding_drafter_amd import make_workspace
+
     g = ds.to_device(case, "cuda")
-    a = run(case, g)
-    b = run(case, g)
+    ws = make_workspace(R, 8, HQ, HKV, STRIDE, "cuda")
+    a = run(case, g, workspace=ws)
+    b = run(case, g, workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(a, b), f"{name}: rerun not bit-identical"
+    # every counter word of every (request, head) line is back at zero
+    assert int(ws[:R * HKV * 256].view(torch.int32).count_nonzero()) == 0
     check(to_np(a), reference(case), name)
