@@ -23,6 +23,8 @@ def _cases():
                                pos_dtype=torch.int64),
         "cfg2": ds.make_config(2),
         "cfg3": ds.make_config(3),
+        # one long request: a plan of more than 16 splits (the two-level combine), fused and replaced
+        "one_long": ds.make_case(1, 8, 24, 4, [20000], seed=63, qknorm=True),
     }
 
 
@@ -46,7 +48,7 @@ def test_kv_append_bit_exact(name):
     assert np.array_equal(g.v_pool.double().cpu().numpy(), v)
 
 
-@pytest.mark.parametrize("name", ["mixed", "qknorm", "cfg2", "cfg3"])
+@pytest.mark.parametrize("name", ["mixed", "qknorm", "cfg2", "cfg3", "one_long"])
 def test_replaced_path_matches_fused_definition(name):
     from speculative_decoding_drafter_amd import drafter_attn, drafter_attn_qknorm, paged_attn, qk_norm_rope
 
