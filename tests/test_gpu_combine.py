@@ -79,3 +79,46 @@ def test_many_split_combine(name):
     # every counter word of every (request, head) line is back at zero
     assert int(ws[:R * HKV * 256].view(torch.int32).count_nonzero()) == 0
     check(to_np(a), reference(case), name)
+
+
+def test_many_split_graph_replays_with_rewritten_lengths():
+    # one captured call of a 64-split plan, replayed with lengths that move the request
+    # between one split, the chunked merge and the two-level merge; every replay equals an
+    # eager call bit for bit (the group counters reset themselves between replays)
+    from speculative_decoding_drafter_amd import drafter_attn_qknorm, make_workspace
+
+    _, ps = _plan()
+    lens_seq = [_lens([64], [7], ps)[0], 100, _lens([12], [3], ps)[0], _lens([17], [0], ps)[0],
+                _lens([40], [5], ps)[0], 64 * 8]
+    case = ds.make_case(R, 8, HQ, HKV, [lens_seq[0]] * R, seed=410, stride=STRIDE, qknorm=True)
+    g = ds.to_device(case, "cuda")
+    ws = make_workspace(R, 8, HQ, HKV, STRIDE, "cuda")
+    out = torch.empty(R * 8, HQ * 64, dtype=torch.bfloat16, device="cuda")
+    kw = dict(num_q_heads=HQ, num_kv_heads=HKV, tokens_per_block=8, scale=case.scale, workspace=ws)
+    args = (g.qkv, g.k_pool, g.v_pool, g.page_table, g.context_lens, g.positions, g.q_norm_weight, g.k_norm_weight)
+    drafter_attn_qknorm(*args, out=out, **kw)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        drafter_attn_qknorm(*args, out=out, **kw)
+    torch.cuda.synchronize()
+    for i, L in enumerate(lens_seq):
+        lens = torch.tensor([L, L // 3, max(0, L - 4000), 7], dtype=torch.int32)
+        g.context_lens.copy_(lens)
+        g.positions.copy_((lens.view(-1, 1) + torch.arange(8)).view(-1).to(g.positions.dtype))
+        say(f"replay {i}: lengths {lens.tolist()}")
+        graph.replay()
+        torch.cuda.synchronize()
+        got = out.clone()
+        eager = drafter_attn_qknorm(*args, **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(got, eager), f"replay {i} differs from an eager call"
+        assert int(ws[:R * HKV * 256].view(torch.int32).count_nonzero()) == 0
+        if i in (0, 4):
+            ref_case = ds.make_case(R, 8, HQ, HKV, lens.tolist(), seed=410, stride=STRIDE, qknorm=True)
+            # the same pool, page table, qkv and weights as the captured case; only lengths/positions differ
+            ref_case.qkv, ref_case.pool, ref_case.page_table = case.qkv, case.pool, case.page_table
+            ref_case.k_pool, ref_case.v_pool = case.k_pool, case.v_pool
+            ref_case.q_norm_weight, ref_case.k_norm_weight = case.q_norm_weight, case.k_norm_weight
+            ref_case.positions = g.positions.cpu()
+            check(to_np(got), reference(ref_case), f"replay-{i}")
