@@ -11,6 +11,8 @@ from .drafter_attn_oracle import (  # noqa: F401
     rope_inv_freq,
     yarn_inv_freq,
     yarn_mscale,
+    yarn_pair_at_turns,
+    YARN_RAMPS,
     gather_context,
     drafter_attn,
     drafter_attn_qknorm,

@@ -73,8 +73,21 @@ def rope_inv_freq(base: float, dim: int = HEAD_DIM) -> np.ndarray:
     return np.power(float(base), -2.0 * i / dim)
 
 
+YARN_RAMPS = ("turns", "index", "index_unrounded")
+
+
+def yarn_pair_at_turns(base: float, original_max_position: float, turns: float, dim: int = HEAD_DIM) -> float:
+    """The (fractional) rotary pair index at which a pair turns exactly ``turns`` times over
+    the original context ``L``: solving ``L * base**(-2i/dim) / (2 pi) = turns`` for ``i``
+    gives ``i = (dim/2) * ln(L / (2 pi turns)) / ln(base)`` (``+inf`` for ``turns = 0``).
+    Pairs below it turn more often, pairs above it less."""
+    if turns <= 0.0:
+        return math.inf
+    return (dim / 2.0) * math.log(float(original_max_position) / (2.0 * math.pi * turns)) / math.log(float(base))
+
+
 def yarn_inv_freq(base: float, factor: float, original_max_position: int, alpha: float = 1.0,
-                  beta: float = 32.0, dim: int = HEAD_DIM) -> np.ndarray:
+                  beta: float = 32.0, dim: int = HEAD_DIM, ramp: str = "turns") -> np.ndarray:
     """YaRN's frequencies ("NTK-by-parts"), for the drafter checkpoint's "YaRN 4.0".
 
     The drafter line of "K3 DFlash Sequence-Compaction GB300 Validation" (Scope and
@@ -82,14 +95,44 @@ def yarn_inv_freq(base: float, factor: float, original_max_position: int, alpha:
     published one (Peng, Quesnelle, Fan, Shippole, "YaRN: Efficient Context Window
     Extension of Large Language Models", 2023, Section 3): for rotary pair ``i`` with
     base frequency ``theta``, the number of turns it makes over the original context
-    is ``r = L * theta / (2 pi)``; ``gamma(r)`` is 0 below ``alpha``, 1 above
-    ``beta`` and linear in ``r`` between them; the new frequency is
+    is ``r = L * theta / (2 pi)``; the weight ``gamma`` of the unscaled frequency is 1
+    for pairs that turn at least ``beta`` times, 0 for pairs that turn at most
+    ``alpha`` times, and ramps between them; the new frequency is
     ``(1 - gamma) * theta / s + gamma * theta``: pairs that turn many times keep their
     frequency, pairs that turn less than ``alpha`` times are interpolated by ``s``.
+
+    ``ramp`` says what the ramp is linear in:
+
+    * ``"turns"`` (the paper's ``gamma(r)``): ``gamma = clamp((r - alpha) / (beta - alpha))``.
+    * ``"index"``: linear in the pair index between ``lo = floor(i(beta))`` and
+      ``hi = ceil(i(alpha))``, where ``i(rho)`` is the fractional index at which a pair
+      turns ``rho`` times (``yarn_pair_at_turns``), both clamped to ``[0, dim/2 - 1]``:
+      ``gamma = 1 - clamp((i - lo) / (hi - lo))``.  The same end points as ``"turns"``
+      (up to the rounding of the bounds to whole pairs), a different shape in between:
+      the parametrisation checkpoint configurations commonly use.
+    * ``"index_unrounded"``: the same with ``lo = i(beta)``, ``hi = i(alpha)`` not rounded.
+
+    Where the clamped bounds meet or cross (``hi <= lo``: an original context so short
+    or so long that the ramp leaves the pair range), pairs up to ``lo`` keep their
+    frequency and the others are interpolated.
     """
+    if ramp not in YARN_RAMPS:
+        raise OracleContractError(f"unknown YaRN ramp {ramp!r}")
     theta = rope_inv_freq(base, dim)
-    turns = float(original_max_position) * theta / (2.0 * math.pi)
-    gamma = np.clip((turns - alpha) / (beta - alpha), 0.0, 1.0)
+    if ramp == "turns":
+        turns = float(original_max_position) * theta / (2.0 * math.pi)
+        gamma = np.clip((turns - alpha) / (beta - alpha), 0.0, 1.0)
+    else:
+        top = dim // 2 - 1
+        lo = min(max(yarn_pair_at_turns(base, original_max_position, beta, dim), 0.0), float(top))
+        hi = min(max(yarn_pair_at_turns(base, original_max_position, alpha, dim), 0.0), float(top))
+        if ramp == "index":
+            lo, hi = float(math.floor(lo)), float(math.ceil(hi))
+        i = np.arange(dim // 2, dtype=np.float64)
+        if hi > lo:
+            gamma = 1.0 - np.clip((i - lo) / (hi - lo), 0.0, 1.0)
+        else:
+            gamma = (i <= lo).astype(np.float64)
     return (1.0 - gamma) * theta / float(factor) + gamma * theta
 
 
@@ -105,8 +148,11 @@ def rope_neox(x: np.ndarray, pos, base: float, yarn: Optional[dict] = None) -> n
     PR #20532, fused_qk_norm_rope drafter cell: NeoX style, base 10000.
     Dimension ``i`` pairs with ``i + dim/2``; the pair is turned by the angle
     ``pos * inv_freq[i]``.  ``pos`` broadcasts against ``x[..., 0]``.  With
-    ``yarn`` (``factor``, ``original_max_position``, optional ``alpha``, ``beta``)
-    the frequencies are YaRN's and the rotated vector is scaled by ``yarn_mscale``.
+    ``yarn`` (``factor``, ``original_max_position``, optional ``alpha`` = 1,
+    ``beta`` = 32, ``ramp`` = ``"turns"`` and ``mscale``) the frequencies are
+    YaRN's and the rotated vector is scaled by ``mscale`` when it is given and
+    positive (a checkpoint that folds the temperature into the softmax scale
+    instead gives 1), else by ``yarn_mscale(factor)``.
     """
     x = np.asarray(x, dtype=np.float64)
     half = x.shape[-1] // 2
@@ -114,8 +160,8 @@ def rope_neox(x: np.ndarray, pos, base: float, yarn: Optional[dict] = None) -> n
         inv_freq, m = rope_inv_freq(base, x.shape[-1]), 1.0
     else:
         inv_freq = yarn_inv_freq(base, yarn["factor"], yarn["original_max_position"], yarn.get("alpha", 1.0),
-                                 yarn.get("beta", 32.0), x.shape[-1])
-        m = yarn_mscale(yarn["factor"])
+                                 yarn.get("beta", 32.0), x.shape[-1], yarn.get("ramp", "turns"))
+        m = float(yarn["mscale"]) if yarn.get("mscale", 0.0) > 0.0 else yarn_mscale(yarn["factor"])
     ang = np.asarray(pos, dtype=np.float64)[..., None] * inv_freq
     c, s = np.cos(ang), np.sin(ang)
     x1, x2 = x[..., :half], x[..., half:]

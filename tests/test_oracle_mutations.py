@@ -4,6 +4,8 @@ Every mutation below is a slip one could make writing the oracle from the
 pages: a dropped term, a wrong sign, index or offset, a transposed operand.
 The pins in test_oracle_pins.py must turn at least one of them red.
 """
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -110,18 +112,52 @@ orig_yfreq = mod.yarn_inv_freq
 orig_mscale = mod.yarn_mscale
 
 
-def _yarn_ramp_reversed(base, factor, L, alpha=1.0, beta=32.0, dim=64):
+orig_pair = mod.yarn_pair_at_turns
+
+
+def _yarn_ramp_reversed(base, factor, L, alpha=1.0, beta=32.0, dim=64, ramp="turns"):
+    if ramp != "turns":
+        return orig_yfreq(base, factor, L, alpha, beta, dim, ramp)
     theta = orig_freq(base, dim)
     g = np.clip((beta - L * theta / (2 * np.pi)) / (beta - alpha), 0.0, 1.0)
     return (1 - g) * theta / factor + g * theta
 
 
-def _yarn_turns_without_2pi(base, factor, L, alpha=1.0, beta=32.0, dim=64):
+def _yarn_turns_without_2pi(base, factor, L, alpha=1.0, beta=32.0, dim=64, ramp="turns"):
+    if ramp != "turns":
+        return orig_yfreq(base, factor, L, alpha, beta, dim, ramp)
     return orig_yfreq(base, factor, L * 2 * np.pi, alpha, beta, dim)
 
 
-def _yarn_times_s(base, factor, L, alpha=1.0, beta=32.0, dim=64):
-    return orig_yfreq(base, 1.0 / factor, L, alpha, beta, dim)
+def _yarn_times_s(base, factor, L, alpha=1.0, beta=32.0, dim=64, ramp="turns"):
+    return orig_yfreq(base, 1.0 / factor, L, alpha, beta, dim, ramp)
+
+
+def _index_ramp(base, factor, L, alpha, beta, dim, round_lo, round_hi, inverted=False):
+    theta = orig_freq(base, dim)
+    lo = round_lo(min(max(orig_pair(base, L, beta, dim), 0.0), dim / 2 - 1))
+    hi = round_hi(min(max(orig_pair(base, L, alpha, dim), 0.0), dim / 2 - 1))
+    i = np.arange(dim // 2)
+    ramp = np.clip((i - lo) / (hi - lo), 0.0, 1.0) if hi > lo else (i > lo).astype(float)
+    g = ramp if inverted else 1.0 - ramp
+    return (1 - g) * theta / factor + g * theta
+
+
+def _yarn_index_rounding_swapped(base, factor, L, alpha=1.0, beta=32.0, dim=64, ramp="turns"):
+    if ramp != "index":
+        return orig_yfreq(base, factor, L, alpha, beta, dim, ramp)
+    return _index_ramp(base, factor, L, alpha, beta, dim, math.ceil, math.floor)
+
+
+def _yarn_index_ramp_inverted(base, factor, L, alpha=1.0, beta=32.0, dim=64, ramp="turns"):
+    if ramp == "turns":
+        return orig_yfreq(base, factor, L, alpha, beta, dim, ramp)
+    rnd = (math.floor, math.ceil) if ramp == "index" else (float, float)
+    return _index_ramp(base, factor, L, alpha, beta, dim, *rnd, inverted=True)
+
+
+def _rope_ignores_mscale(x, pos, base, yarn=None):
+    return orig_rope(x, pos, base, None if yarn is None else {k: v for k, v in yarn.items() if k != "mscale"})
 
 
 def _gather_shift_slot(k_pool, v_pool, row, L, g):
@@ -197,6 +233,11 @@ MUTATIONS = {
     "yarn_multiplies_by_s": ("yarn_inv_freq", _yarn_times_s),
     "yarn_mscale_log10": ("yarn_mscale", lambda f: 0.1 * np.log10(f) + 1.0),
     "yarn_no_mscale": ("yarn_mscale", lambda f: 1.0),
+    "yarn_index_rounding_swapped": ("yarn_inv_freq", _yarn_index_rounding_swapped),
+    "yarn_index_ramp_inverted": ("yarn_inv_freq", _yarn_index_ramp_inverted),
+    "yarn_pair_index_over_full_dim": ("yarn_pair_at_turns", lambda base, L, t, dim=64: orig_pair(base, L, t, 2 * dim)),
+    "yarn_pair_index_without_2pi": ("yarn_pair_at_turns", lambda base, L, t, dim=64: orig_pair(base, L * 2 * math.pi, t, dim)),
+    "yarn_explicit_mscale_ignored": ("rope_neox", _rope_ignores_mscale),
     "merge_no_rescale": ("_merge_parts", _merge_no_rescale),
     "merge_max_of_first_range": ("_merge_parts", _merge_max_of_first),
 }
@@ -220,9 +261,16 @@ def _battery():
     for name in ("test_rmsnorm_closed_forms", "test_rope_closed_forms", "test_qk_norm_rope_closed_forms",
                  "test_qk_norm_rope_constant_heads_at_position_zero", "test_yarn_factor_one_is_plain_rope",
                  "test_yarn_short_original_context_is_position_interpolation",
-                 "test_yarn_long_original_context_only_scales", "test_yarn_ramp_midpoint_and_shape"):
+                 "test_yarn_long_original_context_only_scales", "test_yarn_ramp_midpoint_and_shape",
+                 "test_yarn_ramps_agree_outside_the_ramp", "test_yarn_index_ramp_degenerate_bounds",
+                 "test_yarn_index_ramp_factor_one_and_explicit_mscale"):
         try:
             getattr(pins, name)()
+        except Exception:  # any error is a failed pin
+            failed.append(name)
+    for name in ("test_yarn_index_ramp_bounds_from_turn_counts", "test_yarn_unrounded_index_ramp"):
+        try:
+            getattr(pins, name)(*pins.YARN_INDEX_CASES[0])
         except Exception:  # any error is a failed pin
             failed.append(name)
     for i in (0, 1):

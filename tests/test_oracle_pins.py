@@ -312,6 +312,99 @@ def test_yarn_ramp_midpoint_and_shape():
     assert (r4 == 1.0).any() and (np.abs(r4 - 0.25) < 1e-15).any() and ((r4 > 0.26) & (r4 < 0.99)).any()
 
 
+# ---- YaRN's ramp linear in the pair index (checkpoint configurations).  The bounds are pinned
+# by the turn counts themselves, evaluated directly: the ramp starts at the last pair that turns
+# at least beta times and ends at the first pair that turns at most alpha times; the unrounded
+# bounds are the fractional pairs whose turn count is exactly beta and alpha.
+
+YARN_INDEX_CASES = [(1e4, 4096, 1.0, 32.0), (1e4, 32768, 1.0, 32.0), (5e5, 8192, 2.0, 16.0), (1e4, 300, 0.5, 4.0)]
+
+
+def _turn_counts(base, L):
+    theta = float(base) ** (-np.arange(32) / 32.0)       # base**(-2i/64)
+    return theta, L * theta / (2 * math.pi)
+
+
+@pytest.mark.parametrize("base,L,a,b", YARN_INDEX_CASES)
+def test_yarn_index_ramp_bounds_from_turn_counts(base, L, a, b):
+    s = 4.0
+    i = np.arange(32)
+    theta, r = _turn_counts(base, L)
+    assert np.min(np.abs(r - b)) > 1e-6 and np.min(np.abs(r - a)) > 1e-6   # no pair sits on a bound
+    lo = int(np.nonzero(r >= b)[0].max())
+    hi = int(np.nonzero(r <= a)[0].min())
+    assert 0 < lo < hi < 31
+    ratio = oracle.yarn_inv_freq(base, s, L, a, b, ramp="index") / theta
+    np.testing.assert_allclose(ratio[:lo + 1], 1.0, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(ratio[hi:], 1.0 / s, rtol=0, atol=1e-15)
+    # in between: the straight line from (lo, 1) to (hi, 1/s), one step per pair
+    step = (1.0 - 1.0 / s) / (hi - lo)
+    np.testing.assert_allclose(ratio[lo:hi + 1], 1.0 - step * (i[lo:hi + 1] - lo), rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("base,L,a,b", YARN_INDEX_CASES)
+def test_yarn_unrounded_index_ramp(base, L, a, b):
+    s = 8.0
+    theta, r = _turn_counts(base, L)
+    lo, hi = oracle.yarn_pair_at_turns(base, L, b), oracle.yarn_pair_at_turns(base, L, a)
+    # the fractional pairs turn exactly beta and alpha times
+    for x, want in ((lo, b), (hi, a)):
+        assert abs(L * float(base) ** (-2.0 * x / 64) / (2 * math.pi) - want) < 1e-10 * want
+    ratio = oracle.yarn_inv_freq(base, s, L, a, b, ramp="index_unrounded") / theta
+    inside = np.nonzero((np.arange(32) > lo) & (np.arange(32) < hi))[0]
+    assert len(inside) >= 3
+    np.testing.assert_allclose(ratio[np.arange(32) <= lo], 1.0, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(ratio[np.arange(32) >= hi], 1.0 / s, rtol=0, atol=1e-15)
+    # straight inside, and its extension reaches 1 at lo and 1/s at hi
+    d = np.diff(ratio[inside])
+    np.testing.assert_allclose(d, d[0], rtol=0, atol=1e-14)
+    assert abs(ratio[inside[0]] + d[0] * (lo - inside[0]) - 1.0) < 1e-12
+    assert abs(ratio[inside[0]] + d[0] * (hi - inside[0]) - 1.0 / s) < 1e-12
+
+
+def test_yarn_ramps_agree_outside_the_ramp():
+    s, (base, L, a, b) = 4.0, YARN_INDEX_CASES[0]
+    theta, r = _turn_counts(base, L)
+    f = {k: oracle.yarn_inv_freq(base, s, L, a, b, ramp=k) / theta for k in oracle.YARN_RAMPS}
+    keep, interp = r >= b, r <= a
+    for k in oracle.YARN_RAMPS:
+        np.testing.assert_allclose(f[k][keep], 1.0, rtol=0, atol=1e-15)
+        np.testing.assert_allclose(f[k][interp], 1.0 / s, rtol=0, atol=1e-15)
+    mid = ~(keep | interp)
+    assert np.abs(f["turns"][mid] - f["index"][mid]).max() > 0.05      # different shapes in between
+
+
+def test_yarn_index_ramp_degenerate_bounds():
+    s = 4.0
+    theta = 1e4 ** (-np.arange(32) / 32.0)
+    for ramp in ("index", "index_unrounded"):
+        # every pair turns more than beta times: nothing is scaled (as with the ramp in turns)
+        f = oracle.yarn_inv_freq(1e4, s, 10 ** 7, 1.0, 32.0, ramp=ramp)
+        np.testing.assert_allclose(f / theta, 1.0, rtol=0, atol=1e-15)
+        # no pair turns even alpha times: both bounds clamp to pair 0, which keeps its frequency
+        f = oracle.yarn_inv_freq(1e4, s, 1, 1.0, 32.0, ramp=ramp)
+        assert f[0] == theta[0]
+        np.testing.assert_allclose(f[1:] / theta[1:], 1.0 / s, rtol=0, atol=1e-15)
+    with pytest.raises(oracle.OracleContractError):
+        oracle.yarn_inv_freq(1e4, s, 4096, ramp="dims")
+
+
+def test_yarn_index_ramp_factor_one_and_explicit_mscale():
+    x, pos = _xp()
+    plain = oracle.rope_neox(x, pos, 1e4)
+    for ramp in oracle.YARN_RAMPS:
+        a = oracle.rope_neox(x, pos, 1e4, dict(factor=1.0, original_max_position=4096, ramp=ramp))
+        np.testing.assert_allclose(a, plain, rtol=0, atol=1e-10)
+        # an explicit factor on q and k replaces the temperature 0.1 ln s + 1 (here e: 1.1)
+        y = dict(factor=math.e, original_max_position=4096, ramp=ramp)
+        d = oracle.rope_neox(x, pos, 1e4, y)
+        m = oracle.rope_neox(x, pos, 1e4, dict(y, mscale=0.75))
+        np.testing.assert_allclose(m, d * (0.75 / 1.1), rtol=1e-13, atol=1e-15)
+        # the rotation keeps each pair's length: only the factor changes it
+        np.testing.assert_allclose(np.hypot(m[:, :32], m[:, 32:]), 0.75 * np.hypot(x[:, :32], x[:, 32:]),
+                                   rtol=1e-12)
+
+
 def test_yarn_attention_equals_explicit_steps():
     # the qknorm attention with YaRN == plain attention on q/k normalised and YaRN-rotated first
     yarn = dict(factor=4.0, original_max_position=256)
