@@ -270,18 +270,37 @@ int drafter_qk_norm_rope(void* qkv, int64_t qkv_row_stride, int32_t num_tokens,
  * "K3 DFlash Sequence-Compaction GB300 Validation", Scope and results) and no
  * other parameter, so the caller supplies them.  The method is the published one
  * (Peng, Quesnelle, Fan, Shippole, "YaRN: Efficient Context Window Extension of
- * Large Language Models", 2023, Section 3): for the frequency f_i = base^(-2i/64)
- * of rotary pair i, turns = original_max_position * f_i / (2 pi) and
- * gamma = clamp((turns - alpha) / (beta - alpha), 0, 1); the pair turns at
- * (1 - gamma) * f_i / factor + gamma * f_i, and the rotated q and k are both
- * multiplied by 0.1 * ln(factor) + 1 (the temperature: logits divided by t).
- * factor 1 is the plain rotation, bit for bit.
+ * Large Language Models", 2023, Section 3): rotary pair i (frequency
+ * f_i = base^(-2i/64)) turns r_i = original_max_position * f_i / (2 pi) times over
+ * the original context; a weight gamma_i of its unscaled frequency, 1 for pairs that
+ * turn at least beta times and 0 for pairs that turn at most alpha times, gives the
+ * frequency (1 - gamma_i) * f_i / factor + gamma_i * f_i; the rotated q and k are
+ * both multiplied by mscale (default 0.1 * ln(factor) + 1, the temperature: logits
+ * divided by t).  Between alpha and beta, gamma is linear in
+ *   DA_YARN_RAMP_TURNS (0, the paper's):  gamma_i = clamp((r_i - alpha) / (beta - alpha), 0, 1);
+ *   DA_YARN_RAMP_INDEX (1):  the pair index: with i(rho) = 32 ln(L / (2 pi rho)) / ln(base)
+ *     the fractional pair that turns rho times, lo = floor(i(beta)) and hi = ceil(i(alpha)),
+ *     each clamped to [0, 31], gamma_i = 1 - clamp((i - lo) / (hi - lo), 0, 1) -- the
+ *     shape checkpoint configurations commonly use;
+ *   DA_YARN_RAMP_INDEX_UNROUNDED (2):  the same with lo = i(beta), hi = i(alpha) (clamped,
+ *     not rounded).
+ * Where the clamped bounds meet (hi <= lo), pairs i <= lo keep f_i and the others take
+ * f_i / factor.  factor 1 with the default mscale is the plain rotation, bit for bit.
+ * A zero-filled tail (ramp 0, mscale 0) is the paper's ramp and temperature.
  */
+#define DA_YARN_RAMP_TURNS 0
+#define DA_YARN_RAMP_INDEX 1
+#define DA_YARN_RAMP_INDEX_UNROUNDED 2
+
 typedef struct da_yarn {
   float factor;                  /* >= 1, finite ("YaRN 4.0": 4) */
   int32_t original_max_position; /* >= 1: the context the base rotation was trained on */
   float alpha;                   /* ramp start in turns, >= 0 (published: 1) */
   float beta;                    /* ramp end in turns, > alpha (published: 32) */
+  int32_t ramp;                  /* DA_YARN_RAMP_TURNS, _INDEX or _INDEX_UNROUNDED */
+  float mscale;                  /* factor on the rotated q and k, finite; 0 = 0.1 ln(factor) + 1
+                                    (a checkpoint that folds the temperature into the softmax
+                                    scale passes 1 and that scale as `scale`) */
 } da_yarn;
 
 /*

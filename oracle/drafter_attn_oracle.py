@@ -118,6 +118,8 @@ def yarn_inv_freq(base: float, factor: float, original_max_position: int, alpha:
     """
     if ramp not in YARN_RAMPS:
         raise OracleContractError(f"unknown YaRN ramp {ramp!r}")
+    if ramp != "turns" and not float(base) > 1.0:
+        raise OracleContractError("YaRN ramps in the pair index need base > 1")
     theta = rope_inv_freq(base, dim)
     if ramp == "turns":
         turns = float(original_max_position) * theta / (2.0 * math.pi)

@@ -14,7 +14,11 @@ c_i32p = ctypes.POINTER(ctypes.c_int32)
 class DaYarn(ctypes.Structure):
     """struct da_yarn of the header (YaRN rotary scaling parameters, passed by host pointer)."""
     _fields_ = [("factor", ctypes.c_float), ("original_max_position", ctypes.c_int32),
-                ("alpha", ctypes.c_float), ("beta", ctypes.c_float)]
+                ("alpha", ctypes.c_float), ("beta", ctypes.c_float),
+                ("ramp", ctypes.c_int32), ("mscale", ctypes.c_float)]
+
+
+YARN_RAMPS = {"turns": 0, "index": 1, "index_unrounded": 2}  # DA_YARN_RAMP_* of the header
 
 
 c_yarnp = ctypes.POINTER(DaYarn)

@@ -96,12 +96,14 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // "NTK-by-parts" frequencies and a temperature factor on q and on k).
 struct Rope {
   double log2_base;   // log2(rope_base)
-  double turn_scale;  // YaRN: L / (2 pi) -- turns of a frequency over the original context L
-  double alpha;       // YaRN ramp start (turns)
-  double inv_ramp;    // YaRN: 1 / (beta - alpha)
+  // YaRN's ramp: gamma_i = clamp((x_i - start) * inv_ramp, 0, 1), with x_i the turns of f_i
+  // over the original context (ramp in turns) or -i (ramp in the pair index)
+  double turn_scale;  // ramp in turns: L / (2 pi), the turns of a unit frequency over L
+  double start;       // where gamma leaves 0: alpha (turns), or -hi (pair index)
+  double inv_ramp;    // 1 / (beta - alpha), or 1 / (hi - lo), or huge for a step at lo
   double inv_s;       // YaRN: 1 / factor
-  float mscale;       // YaRN: 0.1 ln(factor) + 1, applied to cos and sin
-  int32_t yarn;       // 0: plain frequencies, no temperature factor
+  float mscale;       // YaRN: the factor on cos and sin
+  int32_t yarn;       // 0: plain frequencies, no factor on cos and sin; 1: ramp in turns; 2: in the pair index
 };
 
 struct Params {
@@ -478,13 +480,15 @@ __device__ __forceinline__ void flag(int32_t* status, int bit) {
 // the angle is formed and reduced modulo 2 pi in fp64 (absolute error about
 // |angle| * 2^-52, 2e-6 rad at positions near 2^33, where fp32 could not even hold
 // the position), then evaluated in fp32.  With YaRN, f_i is first moved towards
-// f_i / s by gamma = clamp((turns - alpha) / (beta - alpha), 0, 1) of its turns over
-// the original context (f_i <- (1 - gamma) f_i / s + gamma f_i), and cos and sin
-// carry the temperature factor.
+// f_i / s: f_i <- (1 - gamma) f_i / s + gamma f_i, with gamma ramping from 0 to 1
+// linearly in the turns f_i makes over the original context or in the pair index
+// (the ramp's constants come from the host), and cos and sin carry the factor on q
+// and k.
 __device__ __forceinline__ float2 rope_cos_sin(int64_t pos, int i, const Rope& rp) {
   double inv_freq = exp2(-static_cast<double>(i) * (1.0 / 32.0) * rp.log2_base);  // base^(-2i/64)
   if (rp.yarn) {
-    const double g = fmin(fmax((rp.turn_scale * inv_freq - rp.alpha) * rp.inv_ramp, 0.0), 1.0);
+    const double x = rp.yarn == 2 ? -static_cast<double>(i) : rp.turn_scale * inv_freq;
+    const double g = fmin(fmax((x - rp.start) * rp.inv_ramp, 0.0), 1.0);
     inv_freq = (1.0 - g) * inv_freq * rp.inv_s + g * inv_freq;
   }
   const double th = static_cast<double>(pos) * inv_freq;
@@ -1506,30 +1510,66 @@ int launch_norm_rope(const NrParams& p, hipStream_t stream) {
   return DA_OK;
 }
 
-int check_yarn(const da_yarn* y) {
+int check_yarn(const da_yarn* y, float rope_base) {
   if (!y) return DA_OK;
   if (!(std::isfinite(y->factor) && y->factor >= 1.f)) return fail(DA_EINVAL, "yarn factor must be finite and >= 1");
   if (y->original_max_position < 1) return fail(DA_EINVAL, "yarn original_max_position must be >= 1");
   if (!(std::isfinite(y->alpha) && std::isfinite(y->beta) && y->alpha >= 0.f && y->beta > y->alpha))
     return fail(DA_EINVAL, "yarn alpha and beta must be finite with 0 <= alpha < beta");
+  if (y->ramp != DA_YARN_RAMP_TURNS && y->ramp != DA_YARN_RAMP_INDEX && y->ramp != DA_YARN_RAMP_INDEX_UNROUNDED)
+    return fail(DA_EINVAL, "yarn ramp must be DA_YARN_RAMP_TURNS, DA_YARN_RAMP_INDEX or DA_YARN_RAMP_INDEX_UNROUNDED");
+  if (!(std::isfinite(y->mscale) && y->mscale >= 0.f))
+    return fail(DA_EINVAL, "yarn mscale must be finite and >= 0 (0: the default temperature)");
+  if (y->ramp != DA_YARN_RAMP_TURNS && !(rope_base > 1.f))
+    return fail(DA_EINVAL, "yarn ramps in the pair index need rope_base > 1 (frequencies falling with the pair)");
   return DA_OK;
 }
 
-// The rotation's parameters from the host arguments.  A YaRN factor of 1 is the
-// plain rotation (taken as such, so it gives the same bits).
+// The rotation's parameters from the host arguments.  A YaRN factor of 1 with the
+// default factor on q and k is the plain rotation (taken as such, so it gives the
+// same bits).  For the ramps in the pair index, the pair that turns rho times over
+// the original context L is i(rho) = 32 ln(L / (2 pi rho)) / ln(base) (f_i =
+// base^(-2i/64) solved for L f_i / (2 pi) = rho); the ramp runs from lo = i(beta)
+// down-rounded to hi = i(alpha) up-rounded (or unrounded), both clamped to the
+// pairs 0..31, and is a step after lo where they meet.
 Rope make_rope(float rope_base, const da_yarn* y) {
   Rope r;
   std::memset(&r, 0, sizeof(r));
   r.log2_base = std::log2(static_cast<double>(rope_base));
   r.inv_s = 1.0;
   r.mscale = 1.f;
-  if (y && y->factor != 1.f) {
-    r.yarn = 1;
-    r.turn_scale = static_cast<double>(y->original_max_position) / 6.283185307179586;  // L / (2 pi)
-    r.alpha = y->alpha;
-    r.inv_ramp = 1.0 / (static_cast<double>(y->beta) - static_cast<double>(y->alpha));
-    r.inv_s = 1.0 / static_cast<double>(y->factor);
-    r.mscale = static_cast<float>(0.1 * std::log(static_cast<double>(y->factor)) + 1.0);
+  if (!y) return r;
+  const double s = y->factor;
+  const float m = y->mscale > 0.f ? y->mscale : static_cast<float>(0.1 * std::log(s) + 1.0);
+  if (y->factor == 1.f && m == 1.f) return r;
+  r.yarn = 1;
+  r.inv_s = 1.0 / s;
+  r.mscale = m;
+  const double L = y->original_max_position, alpha = y->alpha, beta = y->beta;
+  constexpr double kTwoPi = 6.283185307179586;
+  if (y->ramp == DA_YARN_RAMP_TURNS) {
+    r.turn_scale = L / kTwoPi;
+    r.start = alpha;
+    r.inv_ramp = 1.0 / (beta - alpha);
+    return r;
+  }
+  const double ln_base = std::log(static_cast<double>(rope_base));
+  auto pair_at = [&](double rho) {
+    const double i = rho > 0.0 ? 32.0 * std::log(L / (kTwoPi * rho)) / ln_base : INFINITY;
+    return std::fmin(std::fmax(i, 0.0), 31.0);
+  };
+  double lo = pair_at(beta), hi = pair_at(alpha);
+  if (y->ramp == DA_YARN_RAMP_INDEX) {
+    lo = std::floor(lo);
+    hi = std::ceil(hi);
+  }
+  r.yarn = 2;
+  if (hi > lo) {  // gamma = clamp((hi - i) / (hi - lo))
+    r.start = -hi;
+    r.inv_ramp = 1.0 / (hi - lo);
+  } else {  // gamma = 1 for pairs i <= lo, else 0
+    r.start = -(std::floor(lo) + 0.5);
+    r.inv_ramp = 0x1p900;
   }
   return r;
 }
@@ -1553,7 +1593,7 @@ int validate_qk(const Common& a, const QkArgs& q, const void* ws, size_t ws_n) {
     return fail(DA_EINVAL, "positions must be aligned to its element size");
   if (!(std::isfinite(q.eps) && q.eps >= 0.f)) return fail(DA_EINVAL, "eps must be finite and >= 0");
   if (!(std::isfinite(q.rope_base) && q.rope_base > 0.f)) return fail(DA_EINVAL, "rope_base must be finite and > 0");
-  const int rc = check_yarn(q.yarn);
+  const int rc = check_yarn(q.yarn, q.rope_base);
   if (rc != DA_OK) return rc;
   if (!aligned16(q.wq) || !aligned16(q.wk)) return fail(DA_EINVAL, "q_norm_weight and k_norm_weight must be 16-byte aligned");
   const size_t out_n = extents(a).out_n;
@@ -1757,7 +1797,7 @@ int drafter_qk_norm_rope_yarn(void* qkv, int64_t qkv_row_stride, int32_t num_tok
     return fail(DA_EINVAL, "positions must be aligned to its element size");
   if (!(std::isfinite(eps) && eps >= 0.f)) return fail(DA_EINVAL, "eps must be finite and >= 0");
   if (!(std::isfinite(rope_base) && rope_base > 0.f)) return fail(DA_EINVAL, "rope_base must be finite and > 0");
-  const int rc = check_yarn(yarn);
+  const int rc = check_yarn(yarn, rope_base);
   if (rc != DA_OK) return rc;
   const size_t qkv_n = static_cast<size_t>(((num_tokens - 1) * qkv_row_stride + width) * 2);
   const size_t pos_n = static_cast<size_t>(num_tokens) * (positions_dtype == DA_POS_INT64 ? 8 : 4);

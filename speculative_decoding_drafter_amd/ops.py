@@ -56,15 +56,20 @@ def make_workspace(num_requests: int, tokens_per_block: int, num_q_heads: int, n
 
 
 def _yarn(yarn: Optional[dict]):
-    """A YaRN parameter dict (``factor``, ``original_max_position``, optional ``alpha`` = 1 and
-    ``beta`` = 32) as the header's host struct, or None."""
+    """A YaRN parameter dict (``factor``, ``original_max_position``, optional ``alpha`` = 1,
+    ``beta`` = 32, ``ramp`` = ``"turns"`` (or ``"index"``, ``"index_unrounded"``) and
+    ``mscale`` = 0, the default temperature) as the header's host struct, or None."""
     if yarn is None:
         return None
     _check(isinstance(yarn, dict) and "factor" in yarn and "original_max_position" in yarn,
-           "yarn must be a dict with factor and original_max_position (alpha, beta optional)")
-    _check(set(yarn) <= {"factor", "original_max_position", "alpha", "beta"}, "unknown yarn parameter")
+           "yarn must be a dict with factor and original_max_position (alpha, beta, ramp, mscale optional)")
+    _check(set(yarn) <= {"factor", "original_max_position", "alpha", "beta", "ramp", "mscale"},
+           "unknown yarn parameter")
+    ramp = yarn.get("ramp", "turns")
+    _check(ramp in _lib.YARN_RAMPS, f"yarn ramp must be one of {sorted(_lib.YARN_RAMPS)}")
     return ctypes.pointer(_lib.DaYarn(float(yarn["factor"]), int(yarn["original_max_position"]),
-                                      float(yarn.get("alpha", 1.0)), float(yarn.get("beta", 32.0))))
+                                      float(yarn.get("alpha", 1.0)), float(yarn.get("beta", 32.0)),
+                                      _lib.YARN_RAMPS[ramp], float(yarn.get("mscale", 0.0))))
 
 
 def _check(cond: bool, msg: str):

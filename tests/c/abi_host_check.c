@@ -22,10 +22,16 @@ int main(void) {
                             (const void*)0x900100, (const void*)0x900200, 1e-5f, 10000.0f, NULL);
   if (rc != DA_EINVAL) { printf("rc %d\n", rc); return 1; }
   /* YaRN parameters travel as a host struct; a factor below 1 is refused before any launch */
-  const da_yarn bad = {0.5f, 4096, 1.0f, 32.0f};
+  const da_yarn bad = {.factor = 0.5f, .original_max_position = 4096, .alpha = 1.0f, .beta = 32.0f};
   rc = drafter_qk_norm_rope_yarn((void*)0x10000, 512, 8, 6, 1, 64, (const void*)0x900000, DA_POS_INT32,
                                  (const void*)0x900100, (const void*)0x900200, 1e-5f, 10000.0f, &bad, NULL);
   if (rc != DA_EINVAL || strstr(drafter_attn_last_error(), "yarn") == NULL) { printf("yarn rc %d\n", rc); return 1; }
+  /* so is a ramp outside DA_YARN_RAMP_* */
+  const da_yarn bad_ramp = {.factor = 4.0f, .original_max_position = 4096, .alpha = 1.0f, .beta = 32.0f,
+                           .ramp = DA_YARN_RAMP_INDEX_UNROUNDED + 1};
+  rc = drafter_qk_norm_rope_yarn((void*)0x10000, 512, 8, 6, 1, 64, (const void*)0x900000, DA_POS_INT32,
+                                 (const void*)0x900100, (const void*)0x900200, 1e-5f, 10000.0f, &bad_ramp, NULL);
+  if (rc != DA_EINVAL || strstr(drafter_attn_last_error(), "ramp") == NULL) { printf("ramp rc %d\n", rc); return 1; }
   /* the no-allocation variant refuses a head_dim of 128 before it touches any device */
   rc = drafter_attn_qknorm_noalloc((const void*)0x10000, 512, (const void*)0x200000, (const void*)0x202000, 16384, 4,
                                    (const int32_t*)0x900000, 1, (const int32_t*)0x900100, NULL, 1, 8, 6, 1, 128, 64,

@@ -277,15 +277,32 @@ def test_small_arrays_must_be_aligned_to_their_elements(lib):
     (4.0, 4096, 5.0, 2.0),               # reversed ramp
     (4.0, 4096, -1.0, 32.0),
     (4.0, 4096, 1.0, float("nan")),
+    (4.0, 4096, 1.0, 32.0, 3, 0.0),      # ramp outside DA_YARN_RAMP_*
+    (4.0, 4096, 1.0, 32.0, -1, 0.0),
+    (4.0, 4096, 1.0, 32.0, 0, -1.0),     # negative factor on q and k
+    (4.0, 4096, 1.0, 32.0, 1, float("nan")),
+    (4.0, 4096, 1.0, 32.0, 2, float("inf")),
+    (4.0, 4096, 1.0, 32.0, 1, 0.0, 1.0),   # a ramp in the pair index with base 1 (no falling frequencies)
+    (4.0, 4096, 1.0, 32.0, 2, 1.0, 0.5),
 ])
 def test_yarn_parameters_rejected_before_launch(lib, yarn):
-    y = ctypes.pointer(_lib.DaYarn(*yarn))
-    rc = lib.drafter_qk_norm_rope_yarn(0x10000, 512, 8, 6, 1, 64, 0x900000, 0, 0x900100, 0x900200, 1e-5, 1e4, y, None)
+    base = yarn[6] if len(yarn) > 6 else 1e4
+    y = ctypes.pointer(_lib.DaYarn(*yarn[:6]))
+    rc = lib.drafter_qk_norm_rope_yarn(0x10000, 512, 8, 6, 1, 64, 0x900000, 0, 0x900100, 0x900200, 1e-5, base, y, None)
     assert rc == DA_EINVAL and "yarn" in _lib.last_error()
     rc = lib.drafter_attn_qknorm_yarn(0x10000, 512, 0x200000, 0x202000, 16384, 4, 0x900000, 1, 0x900100, None,
-                                      1, 8, 6, 1, 64, 64, 0.125, 0x900200, 0, 0x900300, 0x900400, 1e-5, 1e4, y,
+                                      1, 8, 6, 1, 64, 64, 0.125, 0x900200, 0, 0x900300, 0x900400, 1e-5, base, y,
                                       0xA00000, 1 << 20, 0xB00000, 384, None, None)
     assert rc == DA_EINVAL and "yarn" in _lib.last_error()
+
+
+@pytest.mark.parametrize("ramp,mscale", [(0, 0.0), (1, 1.0), (2, 0.5)])
+def test_acceptable_yarn_passes_the_yarn_checks(lib, ramp, mscale):
+    # an acceptable YaRN struct gets past the YaRN checks: the call then fails on the next
+    # host check (positions inside the qkv rows it would rewrite), before any launch
+    y = ctypes.pointer(_lib.DaYarn(4.0, 4096, 1.0, 32.0, ramp, mscale))
+    rc = lib.drafter_qk_norm_rope_yarn(0x10000, 512, 8, 6, 1, 64, 0x10100, 0, 0x900100, 0x900200, 1e-5, 1e4, y, None)
+    assert rc == DA_EINVAL and "overlaps" in _lib.last_error()
 
 
 def test_binding_rejects_malformed_yarn():
@@ -294,8 +311,11 @@ def test_binding_rejects_malformed_yarn():
 
     assert _yarn(None) is None
     assert _yarn(dict(factor=4.0, original_max_position=4096)).contents.beta == 32.0
+    y = _yarn(dict(factor=4.0, original_max_position=4096, ramp="index_unrounded", mscale=1.0)).contents
+    assert (y.ramp, y.mscale) == (2, 1.0)
     for bad in (dict(factor=4.0), dict(original_max_position=4096), (4.0, 4096),
-                dict(factor=4.0, original_max_position=4096, mscale=2.0)):
+                dict(factor=4.0, original_max_position=4096, ramp="dims"),
+                dict(factor=4.0, original_max_position=4096, rope_type="yarn")):
         with pytest.raises(DrafterAttnError):
             _yarn(bad)
 

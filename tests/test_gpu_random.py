@@ -5,7 +5,7 @@ toward page edges (0, 64k-1, 64k, 64k+1) up to 4 pages past a few hundred,
 a page-table stride at or above the need, ragged block lengths, qknorm or
 plain, int32 or int64 positions with offsets, poison, qkv row padding and
 separate pools; about a third of the qknorm cases use YaRN with drawn
-parameters.  Each must meet the acceptance bar; a rerun must be bit-identical.
+parameters (factor, original context, ramp bounds and shape, factor on q and k).  Each must meet the acceptance bar; a rerun must be bit-identical.
 Also: the binding refuses wrong dtypes and shapes.
 """
 import numpy as np
@@ -47,8 +47,13 @@ def _yarn_draw(i: int, case: ds.DrafterCase):
     if not case.qknorm or rng.random() >= 0.35:
         return None
     a = float(rng.uniform(0.0, 4.0))
-    return dict(factor=float(rng.choice([1.0, 2.0, 4.0, 8.0])), original_max_position=int(rng.choice([256, 4096, 32768])),
-                alpha=a, beta=a + float(rng.uniform(1.0, 64.0)))
+    y = dict(factor=float(rng.choice([1.0, 2.0, 4.0, 8.0])), original_max_position=int(rng.choice([256, 4096, 32768])),
+             alpha=a, beta=a + float(rng.uniform(1.0, 64.0)))
+    # the ramp's shape and the factor on q and k (drawn after the rest, which stays as it was)
+    y["ramp"] = str(rng.choice(["turns", "index", "index_unrounded"]))
+    if rng.random() < 0.3:
+        y["mscale"] = float(rng.uniform(0.5, 2.0))
+    return y
 
 
 @pytest.mark.parametrize("i", range(40))

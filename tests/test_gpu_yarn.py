@@ -7,7 +7,9 @@ caller's (here a 4096-token original context and the published ramp 1..32).
 * factor 1 gives the plain rotation's bits;
 * the standalone op against the oracle within one bf16 ulp plus fp32 rounding, and
   plain attention on its rows == the fused attention, bit for bit;
-* graph replay with rewritten positions equals eager calls, bit for bit.
+* graph replay with rewritten positions equals eager calls, bit for bit;
+* the ramps linear in the pair index (rounded and unrounded bounds) and an explicit
+  factor on q and k, against the oracle, in the attention and the standalone op.
 """
 import numpy as np
 import pytest
@@ -136,3 +138,65 @@ def test_graph_replay_with_rewritten_positions():
         assert torch.equal(replayed.view(torch.int16), eager.view(torch.int16))
         case.positions = g.positions.cpu()
         check(to_np(replayed), _ref(case, YARN), f"yarn-replay{k}")
+
+
+VARIANTS = {
+    "index": dict(YARN, ramp="index"),
+    "index_unrounded": dict(YARN, ramp="index_unrounded", mscale=1.0),
+    "index_mscale": dict(YARN, ramp="index", mscale=1.25),
+    "turns_mscale_one": dict(YARN, mscale=1.0),
+    "factor_one_mscale": dict(factor=1.0, original_max_position=4096, ramp="index", mscale=1.3),
+}
+
+
+@pytest.mark.parametrize("name", ["cfg3", "far_positions"])
+@pytest.mark.parametrize("variant", list(VARIANTS))
+def test_qknorm_yarn_variants_match_oracle(name, variant):
+    case = {
+        "cfg3": lambda: ds.make_config(3),
+        "far_positions": lambda: ds.make_case(3, 8, 24, 4, [300, 0, 1500], seed=41, qknorm=True,
+                                              pos_dtype=torch.int64, pos_offset=[100000, 7, 3_000_000]),
+    }[name]()
+    yarn = VARIANTS[variant]
+    g = ds.to_device(case, "cuda")
+    say(f"yarn {variant} {name}")
+    got = to_np(_fused(case, g, yarn))
+    ref = _ref(case, yarn)
+    check(got, ref, f"yarn-{variant}-{name}")
+    # the variant really changes the answer: the default YaRN rotation's result would fail the bar
+    other = _ref(case, YARN if variant != "factor_one_mscale" else None)
+    err = np.abs(other - ref)
+    assert err.mean() > MEAN_TOL or np.any(err > ATOL + RTOL * np.abs(ref))
+
+
+def test_index_ramp_factor_one_is_the_plain_rotation_bitwise():
+    case = ds.make_config(2)
+    g = ds.to_device(case, "cuda")
+    say("yarn index ramp, factor 1")
+    plain = _fused(case, g, None)
+    for ramp in ("index", "index_unrounded"):
+        one = _fused(case, g, dict(factor=1.0, original_max_position=4096, ramp=ramp))
+        torch.cuda.synchronize()
+        assert torch.equal(plain.view(torch.int16), one.view(torch.int16)), ramp
+
+
+@pytest.mark.parametrize("variant", ["index", "index_unrounded", "factor_one_mscale"])
+def test_norm_rope_yarn_variants_match_oracle(variant):
+    from speculative_decoding_drafter_amd import qk_norm_rope
+
+    yarn = VARIANTS[variant]
+    rows = ds.make_norm_rope_rows(131, 4, seed=640, row_pad=8, pos_dtype=torch.int64, pos_max=1 << 22)
+    say(f"norm_rope yarn {variant}")
+    got = qk_norm_rope(rows.qkv.cuda(), rows.positions.cuda(), rows.q_norm_weight.cuda(), rows.k_norm_weight.cuda(),
+                       num_q_heads=rows.Hq, num_kv_heads=rows.Hkv, yarn=yarn).cpu()
+    ref = oracle.qk_norm_rope(rows.qkv.double().numpy(), rows.positions.numpy(), rows.q_norm_weight.double().numpy(),
+                              rows.k_norm_weight.double().numpy(), num_q_heads=rows.Hq, num_kv_heads=rows.Hkv,
+                              yarn=yarn)
+    qk = slice(0, (rows.Hq + rows.Hkv) * 64)
+    gq, rq = got[:, qk].double().numpy(), ref[:, qk]
+    head_max = np.abs(rq).reshape(rq.shape[0], -1, 64).max(axis=2, keepdims=True)
+    fp32 = np.ldexp(np.broadcast_to(head_max, (rq.shape[0], rq.shape[1] // 64, 64)).reshape(rq.shape), -18)
+    bound = np.maximum(_bf16_ulp(rq), _bf16_ulp(gq)) + fp32
+    err = np.abs(gq - rq)
+    say(f"max |err|/bound = {np.max(err / bound):.3f}")
+    assert np.isfinite(gq).all() and np.all(err <= bound)
