@@ -387,6 +387,10 @@ def test_yarn_index_ramp_degenerate_bounds():
         np.testing.assert_allclose(f[1:] / theta[1:], 1.0 / s, rtol=0, atol=1e-15)
     with pytest.raises(oracle.OracleContractError):
         oracle.yarn_inv_freq(1e4, s, 4096, ramp="dims")
+    # with base <= 1 the frequencies do not fall along the pairs: no index ramp
+    for base in (1.0, 0.5):
+        with pytest.raises(oracle.OracleContractError):
+            oracle.yarn_inv_freq(base, s, 4096, ramp="index")
 
 
 def test_yarn_index_ramp_factor_one_and_explicit_mscale():
