@@ -285,7 +285,10 @@ int drafter_qk_norm_rope(void* qkv, int64_t qkv_row_stride, int32_t num_tokens,
  *   DA_YARN_RAMP_INDEX_UNROUNDED (2):  the same with lo = i(beta), hi = i(alpha) (clamped,
  *     not rounded).
  * Where the clamped bounds meet (hi <= lo), pairs i <= lo keep f_i and the others take
- * f_i / factor.  factor 1 with the default mscale is the plain rotation, bit for bit.
+ * f_i / factor.  The index ramps need rope_base > 1 (frequencies falling along the
+ * pairs); a ramp outside the three, a negative or non-finite mscale, or an index ramp
+ * with rope_base <= 1 returns DA_EINVAL.  factor 1 with the default mscale is the plain
+ * rotation, bit for bit.
  * A zero-filled tail (ramp 0, mscale 0) is the paper's ramp and temperature.
  */
 #define DA_YARN_RAMP_TURNS 0
